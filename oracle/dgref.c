@@ -1,0 +1,238 @@
+/*
+ * dgref.c -- CPU oracle for the FP8 block-scaled NT GEMM (dense, contiguous-grouped,
+ * masked-grouped).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call this
+ * file; only the tests, the smoke check and the benchmark's CPU-baseline leg do.  It
+ * shares no code, header, table or helper with the GPU library.
+ *
+ * What it computes (the method's own definition, written out plainly):
+ *
+ *   C[m,n] = bf16_rne( sum_kb  sA[m,kb] * sB_g[n/128, kb] *
+ *                      sum_{k in block kb}  dec(A[m,k]) * dec(B_g[n,k]) )
+ *
+ *   - NT layout: A is M x K row-major, B is stored N x K row-major (the RHS is
+ *     transposed); DeepGEMM page on turtlesai.it, technical summary paragraph.
+ *   - fine-grained scaling: one fp32 scale per 1x128 block of A and per 128x128 block
+ *     of B; same paragraph ("ridimensionamento a grana fine") and the chattools.cn
+ *     article, section on core design ideas.
+ *   - two-level accumulation: each 128-deep K block is summed on its own, scaled, and
+ *     then added into a separate higher-precision accumulator (same two sources).
+ *   - BF16 output: aisharenet.com/ja usage guide, section "basic FP8 GEMM".
+ *   - grouping on M only, experts share N and K: aisharenet.com/ja usage guide,
+ *     section on grouped GEMM for MoE; contiguous and masked layouts: flashmla.org/zh
+ *     page, section "DeepGEMM performance", and the usage guide's sections 2 and 3.
+ *
+ * Precision: the block partial is summed in fp64 and is exact (each e4m3 product has
+ * at most 8 significant bits and magnitude in [2^-18, 448^2]; 128 of them stay below
+ * 2^25, i.e. within 43 bits).  sA*sB is exact in fp64 (24+24 bits).  The scaled term
+ * is rounded once to fp64, the K-block sum runs in fp64 in kb order 0,1,2,..., and the
+ * result is rounded once, directly from fp64, to bf16 with round-to-nearest-even.
+ *
+ * Readings where the pages are silent (each one is listed with its reason in the
+ * design notes of this repository):
+ *   - K need not be a multiple of 128 here: the last block is short and uses scale
+ *     column floor(k/128).
+ *   - N need not be a multiple of 128: sB has ceil(N/128) rows; column n uses row n/128.
+ *   - contiguous routing: row m is written iff 0 <= group_idx[m] < G and
+ *     group_idx[m] == group_idx[128*floor(m/128)]; other rows are left untouched.
+ *   - masked routing: group g writes rows [0, clamp(masked_m[g], 0, cap)); all other
+ *     rows of C are left untouched, and A rows past that count are never read.
+ *
+ * Parity pins live in tests/ (worked example, exact-rational brute force, integer
+ * inputs, power-of-two scaling, group-order independence, untouched masked rows,
+ * reductions between the three forms, NumPy fp64 matmul with unit scales).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define DGREF_BLOCK 128
+
+/* OCP 8-bit floating point, E4M3 ("fn": finite, no infinities).  Sign bit, 4-bit
+ * exponent with bias 7, 3-bit mantissa.  Exponent field 0 is subnormal: m * 2^-9.
+ * S.1111.111 is NaN; every other code is finite; the largest is 0x7E = 448. */
+double dgref_e4m3fn_decode(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);                 /* 0.m * 2^(1-7) */
+    else
+        v = ldexp((double)(8 + m), e - 10);       /* 1.m * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest bf16 (8 significant bits, 8 exponent bits, bias 127),
+ * ties to even, in one step from the double value.  NaN -> 0x7FC0.  Overflow past the
+ * largest finite bf16 rounds to infinity, as round-to-nearest requires. */
+uint16_t dgref_bf16_rne(double x)
+{
+    union { float f; uint32_t u; } cv;
+    double ax, q, r, fl, y;
+    int e;
+    if (isnan(x))
+        return 0x7FC0;
+    ax = fabs(x);
+    if (ax == 0.0) {
+        cv.f = (float)x;                          /* keeps the sign of zero */
+        return (uint16_t)(cv.u >> 16);
+    }
+    frexp(ax, &e);                                /* ax = f * 2^e, f in [0.5, 1) */
+    if (e < -125)
+        e = -125;                                 /* subnormal bf16: fixed quantum 2^-133 */
+    q = ldexp(1.0, e - 8);                        /* spacing of bf16 values near ax */
+    r = ax / q;                                   /* exact: division by a power of two */
+    fl = floor(r);
+    if (r - fl > 0.5 || (r - fl == 0.5 && fmod(fl, 2.0) != 0.0))
+        fl += 1.0;
+    y = fl * q;
+    if (y >= ldexp(1.0, 128))
+        return (uint16_t)(x < 0 ? 0xFF80 : 0x7F80);
+    cv.f = (float)(x < 0 ? -y : y);               /* exact: y has at most 8 significant bits */
+    return (uint16_t)(cv.u >> 16);
+}
+
+static double g_dec[256];
+static int g_dec_ready = 0;
+
+static void build_decode_table(void)
+{
+    int c;
+    if (g_dec_ready)
+        return;
+    for (c = 0; c < 256; ++c)
+        g_dec[c] = dgref_e4m3fn_decode((uint8_t)c);
+    g_dec_ready = 1;
+}
+
+/* The unrounded fp64 result of one output element: the two-level sum above. */
+static double element_f64(const uint8_t *a_row, const float *sa_row,
+                          const uint8_t *b_row, const float *sb_row, int64_t K)
+{
+    int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
+    double acc = 0.0;
+    int64_t kb, k;
+    for (kb = 0; kb < nkb; ++kb) {
+        int64_t k0 = kb * DGREF_BLOCK;
+        int64_t k1 = k0 + DGREF_BLOCK < K ? k0 + DGREF_BLOCK : K;
+        double partial = 0.0;
+        double s;
+        for (k = k0; k < k1; ++k)
+            partial += g_dec[a_row[k]] * g_dec[b_row[k]];
+        s = (double)sa_row[kb] * (double)sb_row[kb];
+        acc += partial * s;
+    }
+    return acc;
+}
+
+/* One output row against one group's B.  acc_out (optional) receives the unrounded
+ * fp64 values, c_out (optional) the bf16 bits. */
+static void one_row(const uint8_t *a_row, const float *sa_row, const uint8_t *B,
+                    const float *sB, int64_t N, int64_t K, uint16_t *c_out, double *acc_out)
+{
+    int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
+    int64_t n;
+    for (n = 0; n < N; ++n) {
+        const uint8_t *b_row = B + n * K;
+        const float *sb_row = sB + (n / DGREF_BLOCK) * nkb;
+        double v = element_f64(a_row, sa_row, b_row, sb_row, K);
+        if (acc_out)
+            acc_out[n] = v;
+        if (c_out)
+            c_out[n] = dgref_bf16_rne(v);
+    }
+}
+
+int dgref_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Dense: C (M x N bf16) = A (M x K) x B (N x K)^T with the block scales.
+ * acc (optional, M x N doubles) receives the unrounded values. */
+void dgref_gemm_fp8_nt(const uint8_t *A, const float *sA, const uint8_t *B,
+                       const float *sB, uint16_t *C, double *acc,
+                       int64_t M, int64_t N, int64_t K)
+{
+    int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
+    int64_t m;
+    build_decode_table();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m)
+        one_row(A + m * K, sA + m * nkb, B, sB, N, K,
+                C ? C + m * N : 0, acc ? acc + m * N : 0);
+}
+
+/* Contiguous grouped: rows of all groups concatenated (M_total x K); B is G x N x K,
+ * sB is G x ceil(N/128) x ceil(K/128); group_idx is one int32 per row. */
+void dgref_grouped_contiguous(const uint8_t *A, const float *sA, const uint8_t *B,
+                              const float *sB, const int32_t *group_idx, uint16_t *C,
+                              double *acc, int64_t M_total, int64_t N, int64_t K,
+                              int64_t G)
+{
+    int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
+    int64_t nnb = (N + DGREF_BLOCK - 1) / DGREF_BLOCK;
+    int64_t m;
+    build_decode_table();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M_total; ++m) {
+        int32_t g = group_idx[m];
+        int32_t lead = group_idx[(m / DGREF_BLOCK) * DGREF_BLOCK];
+        if (g < 0 || g >= G || g != lead)
+            continue;                             /* row left untouched */
+        one_row(A + m * K, sA + m * nkb, B + (int64_t)g * N * K, sB + (int64_t)g * nnb * nkb,
+                N, K, C ? C + m * N : 0, acc ? acc + m * N : 0);
+    }
+}
+
+/* Masked grouped: A is G x cap x K, C is G x cap x N; group g computes its first
+ * clamp(masked_m[g], 0, cap) rows and leaves the rest of C untouched. */
+void dgref_grouped_masked(const uint8_t *A, const float *sA, const uint8_t *B,
+                          const float *sB, const int32_t *masked_m, uint16_t *C,
+                          double *acc, int64_t G, int64_t cap, int64_t N, int64_t K)
+{
+    int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
+    int64_t nnb = (N + DGREF_BLOCK - 1) / DGREF_BLOCK;
+    int64_t i;
+    build_decode_table();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < G * cap; ++i) {
+        int64_t g = i / cap, m = i % cap;
+        int64_t valid = masked_m[g];
+        if (valid < 0)
+            valid = 0;
+        if (valid > cap)
+            valid = cap;
+        if (m >= valid)
+            continue;                             /* row left untouched */
+        one_row(A + i * K, sA + i * nkb, B + g * N * K, sB + g * nnb * nkb, N, K,
+                C ? C + i * N : 0, acc ? acc + i * N : 0);
+    }
+}
+
+/* Element-wise helpers for the tests. */
+void dgref_bf16_rne_array(const double *x, uint16_t *out, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i)
+        out[i] = dgref_bf16_rne(x[i]);
+}
+
+void dgref_e4m3fn_decode_array(const uint8_t *codes, double *out, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i)
+        out[i] = dgref_e4m3fn_decode(codes[i]);
+}
