@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 block-scaled NT GEMM on one MI355X.
+
+A step is one pass over every shape of the chosen workload, each shape one call of
+the library on inputs already resident in HBM.  Default workload: the dense decode
+shapes (M in {64,128} x the six DeepSeek-V3 (N,K) pairs of the flashmla.org/zh page's
+dense table), which are bound by HBM bandwidth.  Other workloads (--workload prefill,
+contiguous, masked, small) exist for measurement; the default line is the one reported.
+
+Prints ONE JSON line with: the workload's aggregate throughput (algorithmic bytes per
+second for HBM-bound workloads, FLOP/s for MFMA-bound ones), a roofline object for the
+dominant kernel (its algorithmic bytes or FLOPs per launch over its mean launch time,
+measured with HIP events recorded on the launch stream inside the timed region), and
+the CPU oracle timed on this host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0         # MI355X dense FP8 MFMA (no sparsity)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "contiguous", "masked", "small"])
+    ap.add_argument("--shapes", default="", help="comma-separated subset of shape indices")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=30.0)
+    ap.add_argument("--detail", default="", help="write per-shape details to this JSON file")
+    return ap.parse_args()
+
+
+def workload_cases(name):
+    from moe_grouped_gemm_lhs_amd import inputs as I
+    return {"decode": I.decode_cases, "prefill": I.prefill_cases,
+            "contiguous": I.contiguous_cases, "masked": I.masked_cases,
+            "small": I.small_case}[name]()
+
+
+WORKLOAD_TEXT = {
+    "decode": "dense decode FP8 NT GEMM, M in {64,128} x (N,K) in {(2112,7168),(24576,1536),"
+              "(32768,512),(7168,16384),(4096,7168),(7168,2048)}, 12 shapes",
+    "prefill": "dense prefill FP8 NT GEMM, M=4096 x the six (N,K) pairs, 1% N(0,30) outliers",
+    "contiguous": "contiguous grouped FP8 NT GEMM, {4x8192, 8x4096, 8x random multiples of 128}"
+                  " rows x (N,K) in {(4096,7168),(7168,2048)}",
+    "masked": "masked grouped FP8 NT GEMM, (G,cap) in {(1,1024),(2,512),(4,256)} x "
+              "(N,K) in {(4096,7168),(7168,2048)}, masked_m ~ U[0,cap]",
+    "small": "dense FP8 NT GEMM 128x256x512",
+}
+
+
+def work_of(p):
+    from moe_grouped_gemm_lhs_amd import accounting as acc
+    if p.kind == "dense":
+        return acc.dense_work(p.M, p.N, p.K)
+    if p.kind == "contiguous":
+        return acc.contiguous_work(p.sizes, p.N, p.K)
+    return acc.masked_work(p.masked_m, p.M, p.N, p.K)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU component).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from moe_grouped_gemm_lhs_amd import binding as dg
+    from moe_grouped_gemm_lhs_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dg.load_library()
+
+    cases = workload_cases(args.workload)
+    if args.shapes:
+        keep = [int(s) for s in args.shapes.split(",")]
+        cases = [cases[i] for i in keep]
+
+    # ---- inputs: generated on the host, made resident in HBM before timing
+    t0 = time.time()
+    problems, calls = [], []
+    for case in cases:
+        p = I.make(case)
+        nkb, nnb = p.K // 128, -(-p.N // 128)
+        A = torch.from_numpy(p.A).to(dev)
+        sA = torch.from_numpy(p.sA).to(dev)
+        B = torch.from_numpy(p.B).to(dev)
+        sB = torch.from_numpy(p.sB).to(dev)
+        if p.kind == "dense":
+            B, sB = B.view(p.N, p.K), sB.view(nnb, nkb)
+            C = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
+            fn = (lambda A=A, sA=sA, B=B, sB=sB, C=C: dg.dg_gemm_fp8_nt(A, sA, B, sB, C))
+        elif p.kind == "contiguous":
+            B, sB = B.view(p.G, p.N, p.K), sB.view(p.G, nnb, nkb)
+            gi = torch.from_numpy(p.group_idx).to(dev)
+            C = torch.empty((p.rows, p.N), dtype=torch.bfloat16, device=dev)
+            fn = (lambda A=A, sA=sA, B=B, sB=sB, gi=gi, C=C:
+                  dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, gi, C))
+        else:
+            A, sA = A.view(p.G, p.M, p.K), sA.view(p.G, p.M, nkb)
+            B, sB = B.view(p.G, p.N, p.K), sB.view(p.G, nnb, nkb)
+            mm = torch.from_numpy(p.masked_m).to(dev)
+            C = torch.empty((p.G, p.M, p.N), dtype=torch.bfloat16, device=dev)
+            fn = (lambda A=A, sA=sA, B=B, sB=sB, mm=mm, C=C:
+                  dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, mm, C))
+        flops, nbytes = work_of(p)
+        kind_id = {"dense": 0, "contiguous": 1, "masked": 2}[p.kind]
+        inst = dg.dg_instance_name(kind_id, p.M if p.kind != "contiguous" else p.rows, p.N, p.K, p.G)
+        problems.append(p)
+        calls.append(dict(name=I.case_name(case), fn=fn, flops=flops, bytes=nbytes,
+                          instance=inst))
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    print(f"[bench] {len(calls)} shapes resident in HBM ({gen_s:.1f} s to generate)",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        for c in calls:
+            c["fn"]()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps; HIP events around every launch on the launch stream
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in calls] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        for i, c in enumerate(calls):
+            ev[s][i][0].record(stream)
+            c["fn"]()
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    wall_s = t_end - t_start
+    ms_per_step = wall_s * 1e3 / args.steps
+
+    per = []
+    for i, c in enumerate(calls):
+        times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        us = 1e3 * float(np.mean(times))
+        per.append(dict(name=c["name"], instance=c["instance"], us=round(us, 3),
+                        us_median=round(1e3 * float(np.median(times)), 3),
+                        tflops=round(c["flops"] / us / 1e6, 2),
+                        gbs=round(c["bytes"] / us / 1e3, 1)))
+    total_flops = sum(c["flops"] for c in calls)
+    total_bytes = sum(c["bytes"] for c in calls)
+    step_s = ms_per_step / 1e3
+    hbm_bound = args.workload in ("decode", "masked", "small")
+    if hbm_bound:
+        value, unit = total_bytes / step_s / 1e9, "GB/s"
+    else:
+        value, unit = total_flops / step_s / 1e12, "TFLOP/s"
+
+    # dominant kernel: the shape with the largest share of the step
+    dom = max(range(len(calls)), key=lambda i: per[i]["us"])
+    d = per[dom]
+    if hbm_bound:
+        achieved = calls[dom]["bytes"] / (d["us"] * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+    else:
+        achieved = calls[dom]["flops"] / (d["us"] * 1e-6) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=FP8_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4), traffic=None)
+    roof["kernel"] = f"{d['instance']} on {d['name']}"
+    roof["launch_us"] = d["us"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(problems, calls, args.cpu_budget_s, hbm_bound)
+
+    line = {
+        "metric": "FP8 TFLOPS and HBM GB/s (as % of MI355X peak) per M,N,K / group shape",
+        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic (seeded N(0,1), 1x128 / 128x128 e4m3fn block quantisation)",
+        "config": {"workload": WORKLOAD_TEXT[args.workload], "shapes": len(calls),
+                   "parallelism": "single GPU"},
+        "tflops": round(total_flops / step_s / 1e12, 2),
+        "gbs": round(total_bytes / step_s / 1e9, 1),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_shape": [[q["name"], q["us"], q["tflops"], q["gbs"]] for q in per],
+    }
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump(dict(line=line, per_shape=per), f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(problems, calls, budget_s, hbm_bound):
+    """Time the CPU oracle on a bounded sample of the workload: whole shapes in order
+    while the budget lasts, else the leading rows of a shape; throughput is scaled to
+    the metric's unit from the work actually done."""
+    import oracle
+    from moe_grouped_gemm_lhs_amd import accounting as acc
+
+    done_s, done_flops, done_bytes, parts = 0.0, 0, 0, []
+    for p, c in zip(problems, calls):
+        if done_s >= budget_s:
+            break
+        if p.kind != "dense":
+            rows = p.rows if p.kind == "contiguous" else p.G * p.M
+        else:
+            rows = p.M
+        # estimate from one small slice first: never overrun the budget by much
+        r_probe = min(rows, max(1, oracle.threads()))
+        t = time.perf_counter()
+        _oracle_rows(p, r_probe)
+        dt = time.perf_counter() - t
+        per_row = dt / r_probe
+        r = int(min(rows, max(r_probe, (budget_s - done_s - dt) / max(per_row, 1e-9))))
+        if r > r_probe:
+            t = time.perf_counter()
+            _oracle_rows(p, r)
+            dt = time.perf_counter() - t
+        else:
+            r = r_probe
+        done_s += dt
+        f, b = acc.flops(r, p.N, p.K), acc.algorithmic_bytes(r, p.N, p.K, 1)
+        done_flops += f
+        done_bytes += b
+        parts.append(f"{c['name']}:{r}/{rows} rows")
+    if hbm_bound:
+        value, unit = done_bytes / done_s / 1e9, "GB/s"
+    else:
+        value, unit = done_flops / done_s / 1e12, "TFLOP/s"
+    return {"value": round(value, 4), "unit": unit, "cores": oracle.threads(), "kind": "oracle",
+            "sample": "; ".join(parts) + f" ({done_s:.1f} s of oracle time)",
+            "tflops": round(done_flops / done_s / 1e12, 5)}
+
+
+def _oracle_rows(p, r):
+    import oracle
+    nnb = -(-p.N // 128)
+    if p.kind == "dense":
+        return oracle.gemm_fp8_nt(p.A[:r], p.sA[:r], p.B, p.sB)
+    if p.kind == "contiguous":
+        return oracle.grouped_contiguous(p.A[:r], p.sA[:r], p.B, p.sB, p.group_idx[:r], p.G)
+    return oracle.gemm_fp8_nt(p.A[:r], p.sA[:r], p.B[:p.N], p.sB[:nnb])
+
+
+if __name__ == "__main__":
+    main()

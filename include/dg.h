@@ -1,0 +1,136 @@
+/*
+ * dg.h -- C ABI of libdg, an FP8 (e4m3fn) block-scaled NT GEMM for AMD Instinct
+ * MI355X (gfx950) with BF16 output, in a dense form and two MoE grouped forms.
+ *
+ * What every call computes (for each written output element):
+ *
+ *   C[m,n] = bf16( sum_kb  sA[m,kb] * sB_g[n/128, kb] *
+ *                  sum_{k = 128kb}^{128kb+127}  A[m,k] * B_g[n,k] )
+ *
+ * The operation and its conventions come from the DeepGEMM pages:
+ *   - FP8 inputs, BF16 output; the call names gemm_fp8_fp8_bf16_nt,
+ *     m_grouped_gemm_fp8_fp8_bf16_nt_contiguous and ..._masked, and the alignment
+ *     query get_m_alignment_for_contiguous_layout: aisharenet.com/ja usage guide,
+ *     sections 1-3 of "main functions".
+ *   - NT layout only (LHS not transposed, RHS transposed, i.e. B stored N x K); casting
+ *     and transposition are the caller's job: turtlesai.it summary, technical paragraph.
+ *   - fine-grained scaling and two-level accumulation: same paragraph, and the
+ *     chattools.cn article, section on core design ideas.  Each 128-deep K block's
+ *     product is formed on its own, multiplied by sA*sB and added into a separate fp32
+ *     accumulator; the result is rounded to bf16 with round-to-nearest-even.
+ *   - grouping on the M axis only, every group sharing N and K: aisharenet.com/ja usage
+ *     guide, section 2; contiguous layout for training / prefill and masked layout for
+ *     decode, usable under graph capture: flashmla.org/zh page, section "DeepGEMM
+ *     performance".
+ *
+ * Conventions shared by every call:
+ *   - Memory: every pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates and frees nothing.  C is an output the library writes in place.
+ *   - Layouts (all row-major, densely packed):
+ *       A  e4m3fn bytes,   rows x K         sA fp32, rows x (K/128)
+ *       B  e4m3fn bytes,   G x N x K        sB fp32, G x ceil(N/128) x (K/128)
+ *       C  bf16 bits,      rows x N
+ *     e4m3fn is the OCP 8-bit format E4M3 (bias 7, max 448, no infinities, NaN = S.1111.111).
+ *     Column n of C uses row n/128 of its group's sB; N need not be a multiple of 128.
+ *   - Preconditions checked on the host, before any device work, in this order:
+ *       shapes: K > 0 and K % 128 == 0, M/N >= 0, G >= 1, cap >= 0  -> DG_ERR_SHAPE
+ *       an empty output (no rows or N == 0) returns DG_OK without touching anything
+ *       pointers non-NULL                                         -> DG_ERR_NULL
+ *       A, B, C 16-byte aligned; sA, sB, group_idx, masked_m 4-byte -> DG_ERR_ALIGN
+ *       workspace_bytes >= dg_workspace_bytes(...) and workspace
+ *       non-NULL when that is > 0                                 -> DG_ERR_WORKSPACE
+ *       current device is a gfx950 GPU                            -> DG_ERR_DEVICE
+ *     A failed launch returns DG_ERR_HIP.  Values that live in device memory
+ *     (group_idx, masked_m) are never read on the host; their rules are stated per call.
+ *   - Execution: every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     null stream), never synchronises, and performs no host readback, so it may be
+ *     captured in a HIP graph.  Faults inside kernels surface at the caller's next
+ *     synchronisation.  Results are deterministic: the same inputs give the same bits.
+ *   - Workspace: device memory the caller lends for split-K partial sums, at least
+ *     dg_workspace_bytes(...) bytes, 16-byte aligned.  Its first 64 KiB hold arrival
+ *     counters that must be zero before the first use; every call leaves them zero
+ *     again, so one workspace can serve calls of any shape in stream order.  Two calls
+ *     that may run concurrently must not share one workspace.
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int dg_status;
+#define DG_OK 0
+#define DG_ERR_NULL 1
+#define DG_ERR_SHAPE 2
+#define DG_ERR_ALIGN 3
+#define DG_ERR_WORKSPACE 4
+#define DG_ERR_DEVICE 5
+#define DG_ERR_HIP 6
+
+#define DG_DENSE 0
+#define DG_CONTIGUOUS 1
+#define DG_MASKED 2
+
+/* Row alignment that each group's segment must have in the contiguous layout
+ * (aisharenet.com/ja usage guide, section 2: group sizes aligned to the GEMM M block).
+ * Returns 128. */
+int dg_get_m_alignment_for_contiguous_layout(void);
+
+/* Static, human-readable name of a status code ("DG_OK", ...); never NULL. */
+const char *dg_status_string(dg_status status);
+
+/* Workspace bytes the call of kind `kind` (DG_DENSE / DG_CONTIGUOUS / DG_MASKED) needs
+ * for these sizes; rows_or_cap is M, M_total or cap.  0 when none is needed.  Returns
+ * 0 for invalid shapes (the call itself then reports DG_ERR_SHAPE). */
+size_t dg_workspace_bytes(int kind, int64_t rows_or_cap, int64_t N, int64_t K, int64_t G);
+
+/* Name of the kernel instance the call of kind `kind` would use for these sizes
+ * (a static string), or "none" for invalid or empty shapes.  Host-only; for logging
+ * and tests. */
+const char *dg_instance_name(int kind, int64_t rows_or_cap, int64_t N, int64_t K, int64_t G);
+
+/* Dense NT GEMM: C (M x N) = A (M x K) x B (N x K)^T with sA (M x K/128) and
+ * sB (ceil(N/128) x K/128).  Every element of C is written.
+ * (aisharenet.com/ja usage guide, section 1: gemm_fp8_fp8_bf16_nt.) */
+dg_status dg_gemm_fp8_nt(const uint8_t *A, const float *sA,
+                         const uint8_t *B, const float *sB,
+                         uint16_t *C, int64_t M, int64_t N, int64_t K,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Contiguous grouped NT GEMM (MoE training forward / prefill).  The rows of all groups
+ * are concatenated into A (M_total x K); B holds G matrices N x K back to back.
+ * group_idx (DEVICE, M_total int32) names the group of each row.  Segments are
+ * expected to be 128-row aligned (dg_get_m_alignment_for_contiguous_layout); the
+ * defined rule for any content is: row m is written with B[group_idx[m]] iff
+ * 0 <= group_idx[m] < G and group_idx[m] == group_idx[128*floor(m/128)]; every other
+ * row of C is left untouched (so -1 can mark padding rows).  Segments may come in any
+ * group order.  (aisharenet.com/ja usage guide, section 2.) */
+dg_status dg_grouped_gemm_fp8_contiguous(const uint8_t *A, const float *sA,
+                                         const uint8_t *B, const float *sB,
+                                         const int32_t *group_idx, uint16_t *C,
+                                         int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                         void *workspace, size_t workspace_bytes,
+                                         void *stream);
+
+/* Masked grouped NT GEMM (MoE decode).  A is G x cap x K (sA G x cap x K/128), B is
+ * G x N x K, C is G x cap x N.  masked_m (DEVICE, G int32) gives each group's count of
+ * valid leading rows, clamped to [0, cap] on the device; group g writes rows
+ * [0, masked_m[g]) of its C block and never writes the others, and A rows at or past
+ * masked_m[g] are never read (they may hold anything).  Nothing is read back to the
+ * host, so the call can be captured once and replayed with new counts.
+ * (aisharenet.com/ja usage guide, section 3; flashmla.org/zh, "DeepGEMM performance".) */
+dg_status dg_grouped_gemm_fp8_masked(const uint8_t *A, const float *sA,
+                                     const uint8_t *B, const float *sB,
+                                     const int32_t *masked_m, uint16_t *C,
+                                     int64_t G, int64_t cap, int64_t N, int64_t K,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H_ */

@@ -1,0 +1,201 @@
+"""Thin ctypes binding of libdg (include/dg.h), with the same call names.
+
+Argument marshalling only: tensors are checked for dtype, shape, device and
+contiguity, their device pointers and the current HIP stream are passed through, and a
+non-zero status raises ``DGError``.  All arithmetic runs in libdg's HIP kernels; there
+is no fallback, and a missing library raises at load time.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdg.so")
+
+DG_DENSE, DG_CONTIGUOUS, DG_MASKED = 0, 1, 2
+_lib = None
+_lock = threading.Lock()
+_workspaces: dict = {}
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call} failed: {dg_status_string(status)} ({status})")
+
+
+def load_library():
+    """Load libdg.so from the package directory (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m moe_grouped_gemm_lhs_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+        lib.dg_get_m_alignment_for_contiguous_layout.restype = I
+        lib.dg_get_m_alignment_for_contiguous_layout.argtypes = []
+        lib.dg_status_string.restype = ctypes.c_char_p
+        lib.dg_status_string.argtypes = [I]
+        lib.dg_workspace_bytes.restype = SZ
+        lib.dg_workspace_bytes.argtypes = [I, I64, I64, I64, I64]
+        lib.dg_instance_name.restype = ctypes.c_char_p
+        lib.dg_instance_name.argtypes = [I, I64, I64, I64, I64]
+        lib.dg_gemm_fp8_nt.restype = I
+        lib.dg_gemm_fp8_nt.argtypes = [P, P, P, P, P, I64, I64, I64, P, SZ, P]
+        lib.dg_grouped_gemm_fp8_contiguous.restype = I
+        lib.dg_grouped_gemm_fp8_contiguous.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64,
+                                                       P, SZ, P]
+        lib.dg_grouped_gemm_fp8_masked.restype = I
+        lib.dg_grouped_gemm_fp8_masked.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64,
+                                                   P, SZ, P]
+        _lib = lib
+    return _lib
+
+
+def dg_get_m_alignment_for_contiguous_layout() -> int:
+    return int(load_library().dg_get_m_alignment_for_contiguous_layout())
+
+
+def dg_status_string(status: int) -> str:
+    return load_library().dg_status_string(int(status)).decode()
+
+
+def dg_workspace_bytes(kind: int, rows_or_cap: int, N: int, K: int, G: int = 1) -> int:
+    return int(load_library().dg_workspace_bytes(kind, rows_or_cap, N, K, G))
+
+
+def dg_instance_name(kind: int, rows_or_cap: int, N: int, K: int, G: int = 1) -> str:
+    return load_library().dg_instance_name(kind, rows_or_cap, N, K, G).decode()
+
+
+# ------------------------------------------------------------------------ marshalling
+def _bytes_view(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype in (torch.float8_e4m3fn,):
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be uint8 or float8_e4m3fn, got {t.dtype}")
+    return t
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _workspace(kind, rows, N, K, G, device, workspace):
+    need = dg_workspace_bytes(kind, rows, N, K, G)
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    if need == 0:
+        return None, 0
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        # zero filled once; every call leaves it zero filled again
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws, ws.numel()
+
+
+def dg_gemm_fp8_nt(A, sA, B, sB, C=None, *, workspace=None, stream=None):
+    """Dense C (M x N bf16) = A (M x K e4m3) x B (N x K e4m3)^T with block scales."""
+    A, B = _bytes_view(A, "A"), _bytes_view(B, "B")
+    M, K = A.shape
+    N = B.shape[0]
+    dev = A.device
+    nkb, nnb = -(-K // 128), -(-N // 128)
+    _check(A, "A", torch.uint8, (M, K), dev)
+    _check(B, "B", torch.uint8, (N, K), dev)
+    _check(sA, "sA", torch.float32, (M, nkb), dev)
+    _check(sB, "sB", torch.float32, (nnb, nkb), dev)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _check(C, "C", torch.bfloat16, (M, N), dev)
+    ws, wsb = _workspace(DG_DENSE, M, N, K, 1, dev, workspace)
+    st = load_library().dg_gemm_fp8_nt(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
+                                       _ptr(ws), wsb, _stream(dev, stream))
+    if st != 0:
+        raise DGError(st, "dg_gemm_fp8_nt")
+    return C
+
+
+def dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, group_idx, C=None, *, workspace=None,
+                                   stream=None):
+    """Contiguous grouped GEMM: A (M_total x K), B (G x N x K), group_idx (M_total int32)."""
+    A, B = _bytes_view(A, "A"), _bytes_view(B, "B")
+    M, K = A.shape
+    G, N = B.shape[0], B.shape[1]
+    dev = A.device
+    nkb, nnb = -(-K // 128), -(-N // 128)
+    _check(A, "A", torch.uint8, (M, K), dev)
+    _check(B, "B", torch.uint8, (G, N, K), dev)
+    _check(sA, "sA", torch.float32, (M, nkb), dev)
+    _check(sB, "sB", torch.float32, (G, nnb, nkb), dev)
+    _check(group_idx, "group_idx", torch.int32, (M,), dev)
+    if C is None:
+        C = torch.zeros((M, N), dtype=torch.bfloat16, device=dev)
+    _check(C, "C", torch.bfloat16, (M, N), dev)
+    ws, wsb = _workspace(DG_CONTIGUOUS, M, N, K, G, dev, workspace)
+    st = load_library().dg_grouped_gemm_fp8_contiguous(
+        _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(group_idx), _ptr(C), M, N, K, G,
+        _ptr(ws), wsb, _stream(dev, stream))
+    if st != 0:
+        raise DGError(st, "dg_grouped_gemm_fp8_contiguous")
+    return C
+
+
+def dg_grouped_gemm_fp8_masked(A, sA, B, sB, masked_m, C=None, *, workspace=None,
+                               stream=None):
+    """Masked grouped GEMM: A (G x cap x K), B (G x N x K), masked_m (G int32)."""
+    A, B = _bytes_view(A, "A"), _bytes_view(B, "B")
+    G, cap, K = A.shape
+    N = B.shape[1]
+    dev = A.device
+    nkb, nnb = -(-K // 128), -(-N // 128)
+    _check(A, "A", torch.uint8, (G, cap, K), dev)
+    _check(B, "B", torch.uint8, (G, N, K), dev)
+    _check(sA, "sA", torch.float32, (G, cap, nkb), dev)
+    _check(sB, "sB", torch.float32, (G, nnb, nkb), dev)
+    _check(masked_m, "masked_m", torch.int32, (G,), dev)
+    if C is None:
+        C = torch.zeros((G, cap, N), dtype=torch.bfloat16, device=dev)
+    _check(C, "C", torch.bfloat16, (G, cap, N), dev)
+    ws, wsb = _workspace(DG_MASKED, cap, N, K, G, dev, workspace)
+    st = load_library().dg_grouped_gemm_fp8_masked(
+        _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(masked_m), _ptr(C), G, cap, N, K,
+        _ptr(ws), wsb, _stream(dev, stream))
+    if st != 0:
+        raise DGError(st, "dg_grouped_gemm_fp8_masked")
+    return C
+
+
+def group_sizes_to_idx(sizes, device=None) -> torch.Tensor:
+    """Per-row int32 group index of contiguous segments of the given sizes."""
+    sizes = torch.as_tensor(list(sizes), dtype=torch.int64)
+    idx = torch.repeat_interleave(torch.arange(len(sizes), dtype=torch.int32), sizes)
+    return idx.to(device) if device is not None else idx

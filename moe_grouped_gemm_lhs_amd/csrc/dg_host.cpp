@@ -1,0 +1,296 @@
+// dg_host.cpp -- host side of libdg: argument validation, kernel-instance selection and
+// launch for the three calls declared in include/dg.h.
+//
+// Validation is pure host code that touches no device state, so every error code
+// except DG_ERR_DEVICE / DG_ERR_HIP can be produced on a machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "dg.h"
+#include "dg_internal.h"
+
+namespace {
+
+using dg::GemmArgs;
+using dg::Instance;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  int checked;
+  int ok;
+  int num_cus;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+int log_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("DG_LOG");
+    v = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+  }
+  return v;
+}
+
+// Current device must be gfx950; caches the CU count.
+dg_status check_device(int* num_cus) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return DG_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return DG_ERR_DEVICE;
+    }
+    d.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.num_cus = prop.multiProcessorCount;
+    d.checked = 1;
+  }
+  if (!d.ok) return DG_ERR_DEVICE;
+  *num_cus = d.num_cus;
+  return DG_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape rules shared by every call.  rows_or_cap = M, M_total or cap.
+dg_status check_shape(int kind, int64_t rows_or_cap, int64_t N, int64_t K, int64_t G) {
+  if (K <= 0 || K % dg::kBlockK != 0) return DG_ERR_SHAPE;
+  if (rows_or_cap < 0 || N < 0 || G < 1) return DG_ERR_SHAPE;
+  // 32-bit row, column and tile indices inside the kernels
+  if (G > INT32_MAX || rows_or_cap > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
+    return DG_ERR_SHAPE;
+  if (kind == dg::kMasked && rows_or_cap * G > INT32_MAX) return DG_ERR_SHAPE;
+  return DG_OK;
+}
+
+const Instance* find_instance(const char* name) {
+  int n = 0;
+  const Instance* all = dg::instances(&n);
+  for (int i = 0; i < n; ++i)
+    if (strcmp(all[i].name, name) == 0) return &all[i];
+  return nullptr;
+}
+
+constexpr int kAssumedCUs = 256;   // MI355X; selection is host-only and device-free
+
+// Relative time of a tiled launch: full rounds of tiles over the CUs times the tile's
+// area, divided by how efficiently that tile shape runs (bigger tiles re-read less).
+double tile_cost(int64_t rows, int64_t N, int64_t groups, int bm, int bn, double eff) {
+  const int64_t tiles = cdiv(rows, bm) * cdiv(N, bn) * groups;
+  const int64_t rounds = cdiv(tiles, kAssumedCUs);
+  return (double)rounds * bm * bn / eff;
+}
+
+// A stream-K instance holds every row in one tile and needs one arrival counter per
+// (column tile, wave).
+bool stream_fits(const Instance* in, int64_t rows, int64_t N) {
+  if (in->mode == dg::kModeStream)
+    return rows <= in->bm && cdiv(N, in->bn) * (in->threads / 64) <= dg::kCounterSlots;
+  return true;
+}
+
+// Instance selection: the heuristic that maps a problem to a build-time instance.
+// DG_FORCE_INSTANCE=<name> overrides it when the named instance serves the call kind.
+const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_t K,
+                                int64_t G) {
+  const char* forced = getenv("DG_FORCE_INSTANCE");
+  if (forced && *forced) {
+    const Instance* f = find_instance(forced);
+    if (f && f->kind == kind && stream_fits(f, rows_or_cap, N)) return f;
+  }
+  const char* name = nullptr;
+  const int64_t groups = kind == dg::kMasked ? G : 1;
+  switch (kind) {
+    case dg::kDense:
+      // decode-shaped (all rows in one tile): persistent stream-K over the column tiles
+      // and K blocks, as long as the per-wave arrival counters fit their header
+      if (rows_or_cap <= 128 && cdiv(N, 64) * 4 <= dg::kCounterSlots) {
+        // 128-column tiles when every CU gets long runs of K blocks; 64-column tiles
+        // otherwise (fewer contributors per shared tile)
+        const int64_t tiles128 = cdiv(N, 128), nkb = K / dg::kBlockK;
+        const bool wide = tiles128 * nkb >= 16 * kAssumedCUs;
+        if (rows_or_cap <= 64)
+          name = wide ? "dense_64x128_stream" : "dense_64x64_stream";
+        else
+          name = wide ? "dense_128x128_stream" : "dense_128x64_stream";
+        break;
+      }
+      /* fall through */
+    case dg::kContiguous:
+    case dg::kMasked: {
+      const char* pre = kind == dg::kDense ? "dense" : kind == dg::kContiguous ? "contig" : "masked";
+      struct Opt { const char* suffix; int bm, bn; double eff; } opts[] = {
+          {"256x256", 256, 256, 1.0}, {"256x224", 256, 224, 1.0}, {"128x128", 128, 128, 0.6}};
+      double best = 1e300;
+      static char buf[64];
+      for (const Opt& o : opts) {
+        snprintf(buf, sizeof(buf), "%s_%s", pre, o.suffix);
+        if (!find_instance(buf)) continue;
+        const double c = tile_cost(rows_or_cap, N, groups, o.bm, o.bn, o.eff);
+        if (c < best) {
+          best = c;
+          name = find_instance(buf)->name;
+        }
+      }
+      if (kind == dg::kMasked && rows_or_cap <= 64) name = "masked_64x128";
+      break;
+    }
+    default:
+      return nullptr;
+  }
+  return name ? find_instance(name) : nullptr;
+}
+
+void fill_tiles(GemmArgs& a, const Instance* in, int kind) {
+  a.nkb = a.K / dg::kBlockK;
+  a.nnb = (int)cdiv(a.N, dg::kBlockK);
+  a.tiles_m = (int)cdiv(a.rows, in->bm);
+  a.tiles_n = (int)cdiv(a.N, in->bn);
+  a.num_tiles = a.tiles_m * a.tiles_n * (kind == dg::kMasked ? a.G : 1);
+  a.band = a.tiles_m < 4 ? a.tiles_m : 4;
+}
+
+size_t workspace_for(const Instance* in, const GemmArgs& a) {
+  if (!in) return 0;
+  if (in->mode == dg::kModeStream)   // counter header + two partial tiles per workgroup
+    return dg::kCounterBytes + (size_t)dg::kStreamGrid * 2 * in->bm * in->bn * sizeof(float);
+  return 0;
+}
+
+dg_status run(int kind, GemmArgs& a, void* workspace, size_t workspace_bytes, void* stream) {
+  const Instance* in = select_instance(kind, a.rows, a.N, a.K, a.G);
+  if (!in) return DG_ERR_SHAPE;
+  fill_tiles(a, in, kind);
+  const size_t ws = workspace_for(in, a);
+  if (ws > 0) {
+    if (!workspace || workspace_bytes < ws || !aligned(workspace, 16)) return DG_ERR_WORKSPACE;
+    a.counters = (uint32_t*)workspace;
+    a.partial = (float*)((char*)workspace + dg::kCounterBytes);
+  }
+  if (in->mode == dg::kModeStream && (!a.partial || !a.counters))
+    return DG_ERR_WORKSPACE;
+  int num_cus = 0;
+  dg_status st = check_device(&num_cus);
+  if (st != DG_OK) return st;
+  const int grid = in->grid(a, num_cus);
+  if (log_enabled())
+    fprintf(stderr, "[dg] kind=%d rows=%d N=%d K=%d G=%d -> %s grid=%d\n", kind, a.rows, a.N,
+            a.K, a.G, in->name, grid);
+  if (grid <= 0) return DG_OK;
+  (void)hipGetLastError();
+  in->launch(a, grid, (hipStream_t)stream);
+  if (hipGetLastError() != hipSuccess) return DG_ERR_HIP;
+  return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_get_m_alignment_for_contiguous_layout(void) { return dg::kAlignM; }
+
+const char* dg_status_string(dg_status s) {
+  switch (s) {
+    case DG_OK: return "DG_OK";
+    case DG_ERR_NULL: return "DG_ERR_NULL";
+    case DG_ERR_SHAPE: return "DG_ERR_SHAPE";
+    case DG_ERR_ALIGN: return "DG_ERR_ALIGN";
+    case DG_ERR_WORKSPACE: return "DG_ERR_WORKSPACE";
+    case DG_ERR_DEVICE: return "DG_ERR_DEVICE";
+    case DG_ERR_HIP: return "DG_ERR_HIP";
+    default: return "DG_ERR_UNKNOWN";
+  }
+}
+
+size_t dg_workspace_bytes(int kind, int64_t rows_or_cap, int64_t N, int64_t K, int64_t G) {
+  if (kind < dg::kDense || kind > dg::kMasked) return 0;
+  if (kind == dg::kDense) G = 1;
+  if (check_shape(kind, rows_or_cap, N, K, G) != DG_OK) return 0;
+  if (rows_or_cap == 0 || N == 0) return 0;
+  const Instance* in = select_instance(kind, rows_or_cap, N, K, G);
+  if (!in) return 0;
+  GemmArgs a{};
+  a.rows = (int)rows_or_cap;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.G = (int)G;
+  fill_tiles(a, in, kind);
+  return workspace_for(in, a);
+}
+
+const char* dg_instance_name(int kind, int64_t rows_or_cap, int64_t N, int64_t K, int64_t G) {
+  if (kind < dg::kDense || kind > dg::kMasked) return "none";
+  if (kind == dg::kDense) G = 1;
+  if (check_shape(kind, rows_or_cap, N, K, G) != DG_OK)
+    return "none";
+  if (rows_or_cap == 0 || N == 0) return "none";
+  const Instance* in = select_instance(kind, rows_or_cap, N, K, G);
+  return in ? in->name : "none";
+}
+
+dg_status dg_gemm_fp8_nt(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
+                         uint16_t* C, int64_t M, int64_t N, int64_t K, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  dg_status st = check_shape(dg::kDense, M, N, K, 1);
+  if (st != DG_OK) return st;
+  if (M == 0 || N == 0) return DG_OK;
+  if (!A || !sA || !B || !sB || !C) return DG_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(sA, 4) ||
+      !aligned(sB, 4))
+    return DG_ERR_ALIGN;
+  GemmArgs a{};
+  a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C;
+  a.rows = (int)M; a.N = (int)N; a.K = (int)K; a.G = 1;
+  return run(dg::kDense, a, workspace, workspace_bytes, stream);
+}
+
+dg_status dg_grouped_gemm_fp8_contiguous(const uint8_t* A, const float* sA, const uint8_t* B,
+                                         const float* sB, const int32_t* group_idx,
+                                         uint16_t* C, int64_t M_total, int64_t N, int64_t K,
+                                         int64_t G, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  dg_status st = check_shape(dg::kContiguous, M_total, N, K, G);
+  if (st != DG_OK) return st;
+  if (M_total == 0 || N == 0) return DG_OK;
+  if (!A || !sA || !B || !sB || !group_idx || !C) return DG_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(sA, 4) ||
+      !aligned(sB, 4) || !aligned(group_idx, 4))
+    return DG_ERR_ALIGN;
+  GemmArgs a{};
+  a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C; a.group_idx = group_idx;
+  a.rows = (int)M_total; a.N = (int)N; a.K = (int)K; a.G = (int)G;
+  return run(dg::kContiguous, a, workspace, workspace_bytes, stream);
+}
+
+dg_status dg_grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const uint8_t* B,
+                                     const float* sB, const int32_t* masked_m, uint16_t* C,
+                                     int64_t G, int64_t cap, int64_t N, int64_t K,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  dg_status st = check_shape(dg::kMasked, cap, N, K, G);
+  if (st != DG_OK) return st;
+  if (cap == 0 || N == 0) return DG_OK;
+  if (!A || !sA || !B || !sB || !masked_m || !C) return DG_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(sA, 4) ||
+      !aligned(sB, 4) || !aligned(masked_m, 4))
+    return DG_ERR_ALIGN;
+  GemmArgs a{};
+  a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C; a.masked_m = masked_m;
+  a.rows = (int)cap; a.N = (int)N; a.K = (int)K; a.G = (int)G;
+  return run(dg::kMasked, a, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,687 @@
+// dg_kernels.hip -- FP8 (e4m3fn) block-scaled NT GEMM kernels for gfx950 (CDNA4).
+//
+// One templated tile body serves the three forms (dense, contiguous-grouped,
+// masked-grouped); the tile scheduler and the epilogue's row predicate differ.
+// For each output tile and each 128-deep K block kb:
+//   1. the e4m3 bytes of A[m0:m0+BM, kb] and B_g[n0:n0+BN, kb], the scales
+//      sA[m0:m0+BM, kb] and the few sB_g[nb, kb] the tile needs are copied global -> LDS
+//      with the direct-to-LDS loads (global_load_lds_dwordx4 / _dword), STAGES blocks
+//      ahead, so that HBM/L2 traffic for later blocks overlaps the math of this one;
+//   2. each 16x16 sub-tile's fp32 block partial comes from one
+//      v_mfma_f32_16x16x128_f8f6f4 started from zero;
+//   3. the partial is promoted on the VALU, acc += partial * (sA[m,kb] * sB[n/128,kb]),
+//      into a separate fp32 register accumulator: the two-level accumulation of the
+//      DeepGEMM pages (turtlesai.it summary, technical paragraph; chattools.cn, core
+//      design ideas).  MFMA issue and the promotion of the partial from two steps
+//      earlier are interleaved by hand (scheduler fences), so the matrix pipe stays
+//      busy while the VALU works and only three partials are alive at a time;
+//   4. after the last K block the accumulator is rounded to bf16 (nearest-even) and
+//      stored, predicated on the rows the form may write.
+//
+// MFMA operand layout.  v_mfma_f32_16x16x128_f8f6f4 takes 32 bytes per lane for each
+// operand: lane l supplies row l%16 of the first operand and column l%16 of the second,
+// lane group q = l/16 a quarter of the 128-deep block.  Which K positions a (q, byte)
+// slot holds does not matter for a dot product as long as both operands use the same
+// assignment; here lane group q takes 16-byte chunks q and q+4 of the row's block.  B is
+// passed as the first operand and A as the second, so the result lane l holds is
+// C[m = l%16][n = 4(l/16) .. 4(l/16)+3]: one row and four consecutive columns.  Hence a
+// lane needs one sA value per 16-row sub-tile, and stores four bf16 at once.
+//
+// LDS layout of a staged operand: 128 bytes per row = 8 chunks of 16 bytes; chunk c of
+// row r sits in slot c ^ (r & 7), so the eight lanes that read the same chunk of eight
+// consecutive rows hit eight different bank groups.  A direct-to-LDS instruction writes
+// 64 lanes x 16 bytes = 8 rows x 128 bytes contiguously; each lane fetches the global
+// chunk that belongs in its slot.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  // format codes 0/0: both operands e4m3; scale operands 0: no hardware block scaling.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (expcnt/lgkmcnt untouched).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most `ahead` stages (PER loads each) of this wave are still in flight.
+template <int PER, int A>
+__device__ __forceinline__ void wait_stages_ahead(int ahead) {
+  if constexpr (A <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (ahead >= A)
+      wait_vmcnt<A * PER>();
+    else
+      wait_stages_ahead<PER, A - 1>(ahead);
+  }
+}
+
+__device__ __forceinline__ void dma16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ v8i read_frag(const uint8_t* base, int row, int q) {
+  const uint8_t* r = base + row * kBlockK;
+  const v4i lo = *(const v4i*)(r + ((q ^ (row & 7)) << 4));
+  const v4i hi = *(const v4i*)(r + (((q + 4) ^ (row & 7)) << 4));
+  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence waits for
+// every outstanding vector-memory operation, i.e. it would drain the direct-to-LDS loads
+// of all the stages that are meant to stay in flight.  Each wave instead waits for its
+// own loads of the stage it is about to read (wait_stages_ahead) before the barrier.
+// The empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Compile-time shape of one kernel instance.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int STAGES = STAGES_;
+  static constexpr int W = WAVES_M * WAVES_N;
+  static constexpr int NT = 64 * W;
+  static constexpr int WM = BM / WAVES_M;       // rows per wave
+  static constexpr int WN = BN / WAVES_N;       // columns per wave
+  static constexpr int TI = WM / 16;            // 16-row sub-tiles per wave
+  static constexpr int TJ = WN / 16;            // 16-column sub-tiles per wave
+  // 1 KB direct loads (8 rows) per wave per stage; when the 8-row blocks do not split
+  // evenly over the waves, the last loads fill padding rows that are never read
+  static constexpr int A_DMA = (BM / 8 + W - 1) / W;
+  static constexpr int B_DMA = (BN / 8 + W - 1) / W;
+  static constexpr int A_BYTES = A_DMA * W * 8 * kBlockK;
+  static constexpr int B_BYTES = B_DMA * W * 8 * kBlockK;
+  static constexpr int S_FLOATS = 64 * W;       // sA for BM rows, then the tile's sB values
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + 4 * S_FLOATS;
+  static constexpr int PER_STAGE = A_DMA + B_DMA + 1;
+  static constexpr int NBV = (BN + 127) / 128 + 1;   // sB blocks a tile can touch
+  // every wave's columns fall inside one 128-column scale block
+  static constexpr bool ONE_NB =
+      (128 % WN == 0) && ((BN % 128 == 0) || (128 % BN == 0));
+  static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "tile shape");
+  static_assert(BM % 8 == 0 && BN % 8 == 0, "direct-load blocks");
+  static_assert(BM + NBV <= S_FLOATS, "scale slots");
+  static_assert(STAGES >= 2 && (STAGES - 2) * PER_STAGE < 64, "pipeline depth");
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Where one output tile lives, and which rows of it may be computed.
+struct TileRef {
+  int ok;        // 0: nothing to do
+  int g;         // group of the first 128-row block (contiguous) / group (masked)
+  int g2;        // contiguous only: group of the second 128-row block, or -1
+  int m0;        // first row of the tile inside the group's row range
+  int row_base;  // global row (A, sA, C) of the group's row 0
+  int rows;      // rows of this tile that exist (>= 1 when ok)
+  int n0;
+};
+
+template <int KIND, class C>
+__device__ __forceinline__ TileRef locate_tile(const GemmArgs& p, int t) {
+  TileRef r;
+  r.ok = 1;
+  r.g2 = -1;
+  int tm, tn;
+  if (KIND == kMasked) {
+    const int per_g = p.tiles_m * p.tiles_n;
+    r.g = t / per_g;
+    t -= r.g * per_g;
+  } else {
+    r.g = 0;
+  }
+  // grouped raster: bands of `band` row-tiles, column-major inside a band, so that
+  // tiles that run together share A rows and B columns
+  const int band = p.band;
+  const int per_band = band * p.tiles_n;
+  const int b = t / per_band;
+  const int in_band = t - b * per_band;
+  const int rows_in_band = min(band, p.tiles_m - b * band);
+  tm = b * band + in_band % rows_in_band;
+  tn = in_band / rows_in_band;
+  r.m0 = tm * C::BM;
+  r.n0 = tn * C::BN;
+  if (KIND == kMasked) {
+    int valid = p.masked_m[r.g];
+    valid = valid < 0 ? 0 : (valid > p.rows ? p.rows : valid);
+    r.row_base = r.g * p.rows;
+    r.rows = min(C::BM, valid - r.m0);
+    r.ok = r.m0 < valid;
+  } else {
+    r.row_base = 0;
+    r.rows = min(C::BM, p.rows - r.m0);
+    if (KIND == kContiguous) {
+      // the tile holds one or two 128-row blocks; each block's leading index names
+      // the only group its rows may be written with
+      r.g = p.group_idx[r.m0];
+      if (C::BM > kAlignM && r.rows > kAlignM) r.g2 = p.group_idx[r.m0 + kAlignM];
+      if (r.g2 == r.g || r.g2 < 0 || r.g2 >= p.G) r.g2 = -1;
+      if (r.g < 0 || r.g >= p.G) {
+        r.g = r.g2;
+        r.g2 = -1;
+      }
+      r.ok = r.g >= 0;
+    }
+  }
+  r.g = uniform(r.g);
+  r.g2 = uniform(r.g2);
+  r.ok = uniform(r.ok);
+  return r;
+}
+
+// Per (tile, group) values the staging and the math need.
+struct TileCtx {
+  const uint8_t* A;
+  const float* sA;
+  const uint8_t* Bg;
+  const float* sBg;
+  int K, nkb, nnb, N;
+  int a_row0;    // global row of the tile's first row
+  int rows;      // rows of the tile that exist
+  int n0;
+  int nb_first;  // sB block of column n0
+  int wave, lane, wm, wn, q, l16;
+};
+
+// Direct-to-LDS copy of K block kb of the tile into stage `st`.
+template <class C>
+__device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const TileCtx& c, int kb) {
+  const int sub = c.lane >> 3;             // row inside the 8-row block
+  const int ch = (c.lane & 7) ^ sub;       // global chunk for this lane's slot
+#pragma unroll
+  for (int it = 0; it < C::A_DMA; ++it) {
+    const int cb = c.wave * C::A_DMA + it;
+    const int row = min(cb * 8 + sub, c.rows - 1);
+    dma16(c.A + (size_t)(c.a_row0 + row) * c.K + kb * kBlockK + ch * 16, st + cb * 1024);
+  }
+#pragma unroll
+  for (int it = 0; it < C::B_DMA; ++it) {
+    const int cb = c.wave * C::B_DMA + it;
+    const int n = min(c.n0 + cb * 8 + sub, c.N - 1);
+    dma16(c.Bg + (size_t)n * c.K + kb * kBlockK + ch * 16, st + C::A_BYTES + cb * 1024);
+  }
+  const int s = c.wave * 64 + c.lane;
+  const float* src;
+  if (s < C::BM)
+    src = c.sA + (size_t)(c.a_row0 + min(s, c.rows - 1)) * c.nkb + kb;
+  else if (s < C::BM + C::NBV)
+    src = c.sBg + (size_t)min(c.nb_first + s - C::BM, c.nnb - 1) * c.nkb + kb;
+  else
+    src = c.sA + (size_t)c.a_row0 * c.nkb + kb;
+  dma4(src, st + C::A_BYTES + C::B_BYTES + c.wave * 256);
+}
+
+// MFMA block partials of one staged K block, promoted into acc.
+template <class C>
+__device__ __forceinline__ void compute_stage(const uint8_t* __restrict__ st, const TileCtx& c,
+                                              v4f (&acc)[C::TI][C::TJ]) {
+  constexpr int TI = C::TI, TJ = C::TJ, WM = C::WM, WN = C::WN;
+  const uint8_t* As = st;
+  const uint8_t* Bs = st + C::A_BYTES;
+  const float* Ss = (const float*)(st + C::A_BYTES + C::B_BYTES);
+  const int q = c.q, l16 = c.l16;
+
+  v8i af[TI];
+  float sa[TI];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int r = c.wm * WM + 16 * i + l16;
+    af[i] = read_frag(As, r, q);
+    sa[i] = Ss[r];
+  }
+  float sb[TJ];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int nb = min((c.n0 + c.wn * WN + 16 * j) / kBlockK, c.nnb - 1);
+    sb[j] = Ss[C::BM + nb - c.nb_first];
+  }
+  float s_i[TI];
+  if (C::ONE_NB) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) s_i[i] = sa[i] * sb[0];
+  }
+  v8i bf[2];
+  bf[0] = read_frag(Bs, c.wn * WN + l16, q);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // software pipeline: MFMA for step t, promotion of step t-2
+  constexpr int T = TI * TJ;
+  v4f part[T];
+#pragma unroll
+  for (int t = 0; t < T + 2; ++t) {
+    if (t < T) {
+      const int j = t / TI, i = t % TI;
+      if (i == 0 && j + 1 < TJ) bf[(j + 1) & 1] = read_frag(Bs, c.wn * WN + 16 * (j + 1) + l16, q);
+      part[t] = mfma_fp8_16x16x128(bf[j & 1], af[i]);
+    }
+    if (t >= 2) {
+      const int u = t - 2;
+      const int j = u / TI, i = u % TI;
+      const float sc = C::ONE_NB ? s_i[i] : sa[i] * sb[j];
+      acc[i][j] = __builtin_elementwise_fma(part[u], (v4f){sc, sc, sc, sc}, acc[i][j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One K-block step: start the copy of a later block into `next`, then multiply the block
+// staged in `cur`.  The two stage pointers are restrict-qualified so that the compiler
+// knows the reads of `cur` cannot see the copy into `next` and does not wait for it;
+// every copy and every read of the K loop goes through this one call site (the
+// prologue too), so they all carry the same pair of alias scopes.
+template <class C>
+__device__ __forceinline__ void kb_step(uint8_t* __restrict__ next, const uint8_t* __restrict__ cur,
+                                        const TileCtx& cn, bool issue, int kb_next,
+                                        const TileCtx& cc, bool compute,
+                                        v4f (&acc)[C::TI][C::TJ]) {
+  if (issue) issue_stage<C>(next, cn, kb_next);
+  if (compute) compute_stage<C>(cur, cc, acc);
+}
+
+// bf16 (round-to-nearest-even) store of one wave's accumulator sub-tiles; rows at or past
+// `rows` and columns at or past N are not written.
+template <class C>
+__device__ __forceinline__ void store_tile_bf16(const v4f (&acc)[C::TI][C::TJ], uint16_t* C_out,
+                                                int N, int row0, int rows, int n0, int wm, int wn,
+                                                int q, int l16) {
+#pragma unroll
+  for (int i = 0; i < C::TI; ++i) {
+    const int ml = wm * C::WM + 16 * i + l16;
+    if (ml >= rows) continue;
+    uint16_t* crow = C_out + (size_t)(row0 + ml) * N;
+#pragma unroll
+    for (int j = 0; j < C::TJ; ++j) {
+      const int n = n0 + wn * C::WN + 16 * j + 4 * q;
+      const v4f v = acc[i][j];
+      if (((N & 3) == 0) && n + 3 < N) {
+        const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+        const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+        *(uint2*)(crow + n) = make_uint2(lo, hi);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) crow[n + e] = (uint16_t)bf16_rne_bits(v[e]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// The tiled kernel.  Each workgroup walks output tiles (persistent: blockIdx strides over
+// the tile list) and runs the whole K loop for each.
+template <int KIND, class C>
+__global__ void __launch_bounds__(C::NT)
+gemm_fp8_kernel(GemmArgs p) {
+  constexpr int WM = C::WM, WN = C::WN, TI = C::TI, TJ = C::TJ;
+  constexpr int STAGES = C::STAGES, PER = C::PER_STAGE;
+  // The kernel's only LDS variable: a second one would make the compiler tag LDS
+  // accesses with per-variable alias scopes, dropping the restrict scopes that keep it
+  // from waiting on in-flight stage copies (see kb_step).
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * C::STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int wm = wave / C::WAVES_N;
+  const int wn = wave - wm * C::WAVES_N;
+  const int q = lane >> 4;
+  const int l16 = lane & 15;
+  const int K = p.K;
+  const int nkb = p.nkb;
+
+  // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs, so give
+  // each XCD a contiguous run of work items (neighbouring tiles share its L2).
+  const int nwork = p.num_tiles;
+  const int G = gridDim.x;
+  const int xcd_runs = (G % 8 == 0) ? 8 : 1;
+  const int slot = (blockIdx.x % xcd_runs) * (G / xcd_runs) + blockIdx.x / xcd_runs;
+
+  for (int t = slot; t < nwork; t += G) {
+    const TileRef tr = locate_tile<KIND, C>(p, t);
+    if (!tr.ok) continue;
+    const int kb_begin = 0;
+    const int nk = nkb;
+    const int a_row0 = tr.row_base + tr.m0;
+
+    // contiguous layout: up to two passes (one per group present in the tile)
+    for (int pass = 0; pass < 2; ++pass) {
+      const int g = pass == 0 ? tr.g : tr.g2;
+      if (g < 0) break;
+      TileCtx c;
+      c.A = p.A;
+      c.sA = p.sA;
+      c.Bg = p.B + (size_t)g * p.N * K;
+      c.sBg = p.sB + (size_t)g * p.nnb * nkb;
+      c.K = K;
+      c.nkb = nkb;
+      c.nnb = p.nnb;
+      c.N = p.N;
+      c.a_row0 = a_row0;
+      c.rows = tr.rows;
+      c.n0 = tr.n0;
+      c.nb_first = tr.n0 / kBlockK;
+      c.wave = wave;
+      c.lane = lane;
+      c.wm = wm;
+      c.wn = wn;
+      c.q = q;
+      c.l16 = l16;
+
+      wait_vmcnt<0>();   // earlier stores must not be counted as staging loads
+      __syncthreads();   // every wave is done reading the stages of the previous tile
+
+      v4f acc[TI][TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+      // iterations 1-STAGES .. -1 only fill the pipeline (STAGES-1 blocks in flight);
+      // iteration it >= 0 waits for block `it`, starts block it+STAGES-1, multiplies `it`
+      for (int it = 1 - STAGES; it < nk; ++it) {
+        if (it >= 0) {
+          // block `it` has landed once only the blocks issued after it are in flight
+          wait_stages_ahead<PER, STAGES - 2>(min(STAGES - 2, nk - 1 - it));
+          stage_barrier();
+        }
+        const int nxt = it + STAGES - 1;
+        const int cur = it < 0 ? 0 : it;
+        kb_step<C>(smem + (nxt % STAGES) * C::STAGE_BYTES, smem + (cur % STAGES) * C::STAGE_BYTES, c,
+                   nxt < nk, kb_begin + nxt, c, it >= 0, acc);
+      }
+
+      // ---------------------------------------------------------------- epilogue
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int ml = wm * WM + 16 * i + l16;
+        if (ml >= tr.rows) continue;
+        const int row = a_row0 + ml;
+        if (KIND == kContiguous) {
+          const int gi = p.group_idx[row];
+          const int lead = p.group_idx[(row / kAlignM) * kAlignM];
+          if (gi != g || lead != g) continue;
+        }
+        uint16_t* crow = p.C + (size_t)row * p.N;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int n = tr.n0 + wn * WN + 16 * j + 4 * q;
+          const v4f v = acc[i][j];
+          if (((p.N & 3) == 0) && n + 3 < p.N) {
+            const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+            const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+            *(uint2*)(crow + n) = make_uint2(lo, hi);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < p.N) crow[n + e] = (uint16_t)bf16_rne_bits(v[e]);
+          }
+        }
+      }
+      if (KIND != kContiguous) break;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Stream-K kernel for short, wide problems (dense, all rows in one tile: the decode
+// shapes).  The (column tile, K block) iterations, tile-major, are split evenly over the
+// persistent grid, so every CU streams the same share of B whatever the shape, and one
+// load pipeline runs through a workgroup's whole range, across tile boundaries.
+// A tile whose K blocks all fall in one workgroup's range is stored as bf16 directly.
+// A tile shared by several workgroups is reduced deterministically: each contributor
+// writes its fp32 partial (per wave, in fragment order: one contiguous 1 KB block per
+// 16x16 sub-tile) with device-coherent (sc1) stores; after its loop, with every store
+// complete, it bumps the tile's per-wave arrival counter; the wave that arrives last
+// adds the contributors' partials in workgroup order and stores bf16.  A workgroup
+// holds at most two shared tiles: the first and the last of its range.
+template <class C>
+__device__ __forceinline__ long stream_start(long g, long W, long G) { return g * W / G; }
+
+template <class C>
+__global__ void __launch_bounds__(C::NT)
+gemm_fp8_stream_kernel(GemmArgs p) {
+  constexpr int TI = C::TI, TJ = C::TJ, STAGES = C::STAGES, PER = C::PER_STAGE;
+  constexpr int FRAG_FLOATS = 64 * 4;                        // one 16x16 fp32 sub-tile
+  constexpr int WAVE_SLOT = TI * TJ * FRAG_FLOATS;           // one wave's partial
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * C::STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int wm = wave / C::WAVES_N;
+  const int wn = wave - wm * C::WAVES_N;
+  const int q = lane >> 4;
+  const int l16 = lane & 15;
+  const int nkb = p.nkb;
+  const long W = (long)p.num_tiles * nkb;
+  const long G = gridDim.x;
+  const long g = blockIdx.x;
+  const long i_begin = stream_start<C>(g, W, G);
+  const long i_end = stream_start<C>(g + 1, W, G);
+  const int t_first = (int)(i_begin / nkb);
+
+  TileCtx cn, cc;
+  cn.A = p.A;
+  cn.sA = p.sA;
+  cn.Bg = p.B;
+  cn.sBg = p.sB;
+  cn.K = p.K;
+  cn.nkb = nkb;
+  cn.nnb = p.nnb;
+  cn.N = p.N;
+  cn.a_row0 = 0;
+  cn.rows = p.rows;
+  cn.wave = wave;
+  cn.lane = lane;
+  cn.wm = wm;
+  cn.wn = wn;
+  cn.q = q;
+  cn.l16 = l16;
+  cc = cn;
+
+  __amdgpu_buffer_rsrc_t part_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      p.partial, (short)0, (int)((size_t)G * 2 * C::W * WAVE_SLOT * 4), 0x00020000);
+
+  v4f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // Iteration bookkeeping with 32-bit counters only (no division in the loop): the copy
+  // runs STAGES-1 iterations ahead of the math; relative iteration r lives in stage
+  // r % STAGES for both.
+  const int n_iter = (int)(i_end - i_begin);
+  int tn = t_first, kbn = (int)(i_begin - (long)t_first * nkb), sn = 0;   // next copy
+  int tc = tn, kbc = kbn, sc = 0, in_tile = 0;                              // next math
+  int shared_tile[2] = {-1, -1};
+  for (int step = 1 - STAGES; step < n_iter; ++step) {
+    if (step >= 0) {
+      wait_stages_ahead<PER, STAGES - 2>(min(STAGES - 2, n_iter - 1 - step));
+      stage_barrier();
+    }
+    const bool issue = step + STAGES - 1 < n_iter;
+    cn.n0 = tn * C::BN;
+    cn.nb_first = cn.n0 / kBlockK;
+    cc.n0 = tc * C::BN;
+    cc.nb_first = cc.n0 / kBlockK;
+    kb_step<C>(smem + sn * C::STAGE_BYTES, smem + sc * C::STAGE_BYTES, cn, issue, kbn, cc,
+               step >= 0, acc);
+    if (issue) {
+      sn = sn + 1 == STAGES ? 0 : sn + 1;
+      if (++kbn == nkb) {
+        kbn = 0;
+        ++tn;
+      }
+    }
+    if (step < 0) continue;
+    sc = sc + 1 == STAGES ? 0 : sc + 1;
+    ++in_tile;
+    const bool tile_end = kbc == nkb - 1 || step == n_iter - 1;
+    if (++kbc == nkb) kbc = 0;
+    if (!tile_end) continue;
+
+    // tile tc ends here for this workgroup
+    if (in_tile == nkb) {
+      store_tile_bf16<C>(acc, p.C, p.N, 0, p.rows, tc * C::BN, wm, wn, q, l16);
+    } else {
+      const int seg = tc == t_first ? 0 : 1;
+      shared_tile[seg] = tc;
+      const int base = (int)(((g * 2 + seg) * C::W + wave) * WAVE_SLOT) * 4;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          __builtin_amdgcn_raw_buffer_store_b128(acc[i][j], part_rsrc,
+                                                 base + ((i * TJ + j) * 64 + lane) * 16, 0,
+                                                 16 /* sc1: device coherent */);
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    ++tc;
+    in_tile = 0;
+  }
+
+  // hand-off of the shared tiles: all partial stores of this workgroup are complete
+  wait_vmcnt<0>();
+#pragma unroll
+  for (int seg = 0; seg < 2; ++seg) {
+    const int t = shared_tile[seg];
+    if (t < 0) continue;
+    uint32_t* ctr = p.counters + (size_t)t * C::W + wave;
+    unsigned old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = (unsigned)__builtin_amdgcn_readfirstlane((int)old);
+    // contributors: the workgroups whose ranges meet iterations [t*nkb, (t+1)*nkb)
+    const long x0 = (long)t * nkb, x1 = x0 + nkb - 1;
+    const long g_first = ((x0 + 1) * G + W - 1) / W - 1;
+    const long g_last = ((x1 + 1) * G + W - 1) / W - 1;
+    if (old != (unsigned)(g_last - g_first)) continue;   // not the last to arrive
+    v4f sum[TI][TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) sum[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    // contributors in workgroup order, RB at a time so that their loads overlap
+    constexpr int RB = TI * TJ <= 8 ? 4 : 2;
+    for (long g0 = g_first; g0 <= g_last; g0 += RB) {
+      v4f part[RB][TI][TJ];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const long gg = min(g0 + u, g_last);
+        const int sg = (int)(stream_start<C>(gg, W, G) / nkb) == t ? 0 : 1;
+        const int base = (int)(((gg * 2 + sg) * C::W + wave) * WAVE_SLOT) * 4;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+            part[u][i][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                part_rsrc, base + ((i * TJ + j) * 64 + lane) * 16, 0, 16 /* sc1 */);
+      }
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+        if (g0 + u <= g_last) {
+#pragma unroll
+          for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) sum[i][j] += part[u][i][j];
+        }
+    }
+    store_tile_bf16<C>(sum, p.C, p.N, 0, p.rows, t * C::BN, wm, wn, q, l16);
+    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <class C>
+void launch_stream(const GemmArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_fp8_stream_kernel<C>), dim3(grid), dim3(C::NT), 0, stream, a);
+}
+
+// persistent stream grid: one workgroup per CU (at most kStreamGrid), never more
+// workgroups than iterations
+int grid_stream(const GemmArgs& a, int num_cus) {
+  const long work = (long)a.num_tiles * a.nkb;
+  long g = num_cus < kStreamGrid ? num_cus : kStreamGrid;
+  return (int)(work < g ? work : g);
+}
+
+template <int KIND, class C>
+void launch(const GemmArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_fp8_kernel<KIND, C>), dim3(grid), dim3(C::NT), 0, stream, a);
+}
+
+// persistent grid: one workgroup per CU (the LDS budget allows no more), capped by work
+int grid_persistent(const GemmArgs& a, int num_cus) {
+  return a.num_tiles < num_cus ? a.num_tiles : num_cus;
+}
+
+using Big = Cfg<256, 256, 4, 2, 2>;      // 8 waves, 64x128 per wave
+using Big224 = Cfg<256, 224, 4, 2, 2>;   // non-power-of-two columns: 64x112 per wave
+using Mid = Cfg<128, 128, 2, 2, 3>;      // 4 waves, 64x64 per wave
+using Small = Cfg<64, 128, 1, 4, 4>;     // 4 waves, 64x32 per wave, 4 stages
+using Str64 = Cfg<64, 128, 1, 4, 5>;     // stream-K decode: 64 rows x 128 columns
+using Str64n64 = Cfg<64, 64, 1, 4, 8>;   // stream-K decode: 64 rows x 64 columns
+using Str128 = Cfg<128, 128, 1, 4, 4>;   // stream-K decode: 128 rows x 128 columns
+using Str128n64 = Cfg<128, 64, 1, 4, 6>; // stream-K decode: 128 rows x 64 columns
+
+}  // namespace
+
+#define DG_INST(NAME, KIND, C) \
+  Instance { NAME, KIND, C::BM, C::BN, kModeTiled, C::NT, grid_persistent, launch<KIND, C> }
+#define DG_STREAM(NAME, C) \
+  Instance { NAME, kDense, C::BM, C::BN, kModeStream, C::NT, grid_stream, launch_stream<C> }
+
+static const Instance kInstances[] = {
+    DG_INST("dense_256x256", kDense, Big),
+    DG_INST("dense_256x224", kDense, Big224),
+    DG_INST("dense_128x128", kDense, Mid),
+    DG_STREAM("dense_64x128_stream", Str64),
+    DG_STREAM("dense_64x64_stream", Str64n64),
+    DG_STREAM("dense_128x128_stream", Str128),
+    DG_STREAM("dense_128x64_stream", Str128n64),
+    DG_INST("contig_256x256", kContiguous, Big),
+    DG_INST("contig_256x224", kContiguous, Big224),
+    DG_INST("contig_128x128", kContiguous, Mid),
+    DG_INST("masked_256x256", kMasked, Big),
+    DG_INST("masked_128x128", kMasked, Mid),
+    DG_INST("masked_64x128", kMasked, Small),
+};
+
+const Instance* instances(int* count) {
+  *count = (int)(sizeof(kInstances) / sizeof(kInstances[0]));
+  return kInstances;
+}
+
+}  // namespace dg

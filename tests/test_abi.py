@@ -1,0 +1,118 @@
+"""Host-side checks of libdg that need no GPU: the library loads, exports every symbol
+that include/dg.h declares, and its argument validation returns each documented error
+code before touching any device state."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from moe_grouped_gemm_lhs_amd import build, binding
+    if not os.path.exists(binding.LIB_PATH):
+        if not os.path.exists(build.HIPCC):
+            pytest.skip("libdg.so not built and hipcc unavailable")
+        build.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"dg_gemm_fp8_nt", "dg_grouped_gemm_fp8_contiguous", "dg_grouped_gemm_fp8_masked",
+            "dg_get_m_alignment_for_contiguous_layout", "dg_workspace_bytes",
+            "dg_status_string", "dg_instance_name"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_constants_and_strings(lib):
+    from moe_grouped_gemm_lhs_amd import binding as b
+    assert b.dg_get_m_alignment_for_contiguous_layout() == 128
+    want = ["DG_OK", "DG_ERR_NULL", "DG_ERR_SHAPE", "DG_ERR_ALIGN", "DG_ERR_WORKSPACE",
+            "DG_ERR_DEVICE", "DG_ERR_HIP"]
+    assert [b.dg_status_string(i) for i in range(7)] == want
+    assert b.dg_status_string(99) == "DG_ERR_UNKNOWN"
+
+
+A16 = 0x10000        # fake, 16-byte aligned addresses: validation never dereferences
+A4 = 0x20004
+BAD16 = 0x10008
+
+
+def dense(lib, A=A16, sA=A4, B=A16, sB=A4, C=A16, M=64, N=256, K=512):
+    return lib.dg_gemm_fp8_nt(A, sA, B, sB, C, M, N, K, None, 0, None)
+
+
+def test_dense_validation_codes(lib):
+    assert dense(lib, K=100) == 2
+    assert dense(lib, K=0) == 2
+    assert dense(lib, M=-1) == 2
+    assert dense(lib, M=0) == 0          # empty output: nothing to do, pointers unused
+    assert dense(lib, N=0, A=None) == 0
+    assert dense(lib, A=None) == 1
+    assert dense(lib, sB=None) == 1
+    assert dense(lib, C=None) == 1
+    assert dense(lib, A=BAD16) == 3
+    assert dense(lib, C=A16 + 2) == 3
+    assert dense(lib, sA=A4 + 1) == 3
+    assert dense(lib, M=1 << 31) == 2
+
+
+def test_grouped_validation_codes(lib):
+    c = lib.dg_grouped_gemm_fp8_contiguous
+    assert c(A16, A4, A16, A4, A4, A16, 256, 128, 128, 0, None, 0, None) == 2   # G < 1
+    assert c(A16, A4, A16, A4, None, A16, 256, 128, 128, 2, None, 0, None) == 1
+    assert c(A16, A4, A16, A4, A4 + 2, A16, 256, 128, 128, 2, None, 0, None) == 3
+    assert c(A16, A4, A16, A4, A4, A16, 0, 128, 128, 2, None, 0, None) == 0
+    m = lib.dg_grouped_gemm_fp8_masked
+    assert m(A16, A4, A16, A4, A4, A16, 2, 64, 128, 96, None, 0, None) == 2     # K % 128
+    assert m(A16, A4, A16, A4, None, A16, 2, 64, 128, 128, None, 0, None) == 1
+    assert m(A16, A4, A16, A4, A4, BAD16, 2, 64, 128, 128, None, 0, None) == 3
+    assert m(A16, A4, A16, A4, A4, A16, 2, 0, 128, 128, None, 0, None) == 0
+    assert m(A16, A4, A16, A4, A4, A16, 1 << 16, 1 << 16, 128, 128, None, 0, None) == 2
+
+
+def test_workspace_validation(lib):
+    from moe_grouped_gemm_lhs_amd import binding as b
+    need = b.dg_workspace_bytes(0, 64, 256, 512, 1)
+    assert need >= 64 * 1024          # stream-K decode instance: counter header + partials
+    f = lib.dg_gemm_fp8_nt
+    assert f(A16, A4, A16, A4, A16, 64, 256, 512, None, need, None) == 4
+    assert f(A16, A4, A16, A4, A16, 64, 256, 512, A16, need - 1, None) == 4
+    assert f(A16, A4, A16, A4, A16, 64, 256, 512, A16 + 8, need, None) == 4   # alignment
+    assert b.dg_workspace_bytes(0, 4096, 4096, 7168, 1) == 0                  # tiled: none
+
+
+def test_device_check_without_gpu(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid-looking fake pointers would be launched")
+    from moe_grouped_gemm_lhs_amd import binding as b
+    need = b.dg_workspace_bytes(0, 64, 256, 512, 1)
+    assert lib.dg_gemm_fp8_nt(A16, A4, A16, A4, A16, 64, 256, 512, A16, need, None) == 5
+    assert lib.dg_gemm_fp8_nt(A16, A4, A16, A4, A16, 4096, 4096, 512, None, 0, None) == 5
+
+
+def test_instance_selection_is_host_logic(lib):
+    from moe_grouped_gemm_lhs_amd import binding as b
+    assert b.dg_instance_name(0, 0, 128, 128) == "none"
+    assert b.dg_instance_name(0, 64, 128, 100) == "none"
+    for kind, rows, n, k, g in [(0, 64, 2112, 7168, 1), (0, 4096, 7168, 16384, 1),
+                                (1, 32768, 4096, 7168, 4), (2, 256, 7168, 2048, 4)]:
+        name = b.dg_instance_name(kind, rows, n, k, g)
+        assert name != "none"
+        assert ("dense", "contig", "masked")[kind] in name
+        ws = b.dg_workspace_bytes(kind, rows, n, k, g)
+        assert ws >= 0
+    assert b.dg_workspace_bytes(0, 64, 2112, 100, 1) == 0

@@ -1,0 +1,244 @@
+"""GPU parity of libdg against the CPU oracle (needs an MI355X and the built library).
+
+Small cases compare every element; the workload shapes compare sampled rows (the
+oracle computes them one by one) plus the exact set of written rows over the whole
+output.  Floating-point results must satisfy, per written element,
+|C_gpu - C_ref| <= 2^-7 |C_ref| + 1e-3 max|C_ref|; routing and masking (which rows are
+written, and the untouched bits of the others) must match exactly; integer-valued
+inputs must match bit for bit."""
+import os
+
+import numpy as np
+import pytest
+
+from moe_grouped_gemm_lhs_amd import inputs as I
+from tests.helpers import (SENTINEL, assert_within_tolerance, bf16_to_f64, e4m3_codes_of,
+                           read_sections)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from tests import gpu_util as gu  # noqa: E402
+
+
+def check_full(p, what, group_idx=None, masked_m=None):
+    gu.say(f"[case] {what}")
+    c_gpu = gu.run_gpu(p, group_idx=group_idx, masked_m=masked_m)
+    c_ref = gu.oracle_full(p, group_idx=group_idx, masked_m=masked_m)
+    w = gu.written_rows(p, group_idx, masked_m)
+    written = np.repeat(w[:, None], p.N, axis=1)
+    assert_within_tolerance(c_gpu, c_ref, written, what)
+    return c_gpu
+
+
+def check_sampled(p, what, seed=0):
+    gu.say(f"[case] {what} (sampled rows)")
+    c_gpu = gu.run_gpu(p)
+    w = gu.written_rows(p)
+    # routing: exactly the written rows changed; every other row keeps the sentinel
+    untouched = c_gpu[~w]
+    assert np.all(untouched == SENTINEL), f"{what}: rows outside the routing were written"
+    rows = gu.sample_rows(p, w, seed=seed)
+    if rows.size == 0:
+        return
+    c_ref = gu.oracle_rows(p, rows)
+    assert_within_tolerance(c_gpu[rows], c_ref, np.ones_like(c_ref, bool), what)
+
+
+# ----------------------------------------------------------------------- small cases
+def test_smallest_instance_128x256x512():
+    p = I.make_dense(128, 256, 512, seed=0)
+    check_full(p, "dense 128x256x512 seed 0")
+
+
+def test_worked_example_padded_to_one_k_block():
+    fx = read_sections("worked_example_3x2x4.txt")
+    Ap = np.zeros((3, 128)); Ap[:, :2] = fx["A"]
+    Bp = np.zeros((4, 128)); Bp[:, :2] = fx["Bt"]
+    p = I.Problem("dense", 3, 4, 128, 1, e4m3_codes_of(Ap), np.ones((3, 1), np.float32),
+                  e4m3_codes_of(Bp), np.ones((1, 1), np.float32))
+    gu.say("[case] worked example")
+    c = gu.run_gpu(p)
+    assert np.array_equal(bf16_to_f64(c), fx["C"])
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 200, 384), (130, 300, 256),
+                                   (64, 16, 128), (257, 520, 1024), (300, 2112, 640),
+                                   (129, 130, 128), (1000, 1100, 384)])
+def test_dense_ragged(M, N, K):
+    p = I.make_dense(M, N, K, seed=M * 7 + N, outliers=True)
+    check_full(p, f"dense ragged {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("kind", ["dense", "contiguous", "masked"])
+def test_every_instance_on_ragged_problem(kind, monkeypatch):
+    """Force each compiled instance of a kind on one ragged problem."""
+    from moe_grouped_gemm_lhs_amd import binding as b
+    names = set()
+    for rows in (1, 16, 64, 65, 96, 128, 200, 256, 1024, 2000, 4096, 32768):
+        for n, k in ((256, 512), (2112, 7168), (7168, 2048), (24576, 1536), (32768, 512),
+                     (7168, 16384), (4096, 7168)):
+            names.add(b.dg_instance_name(("dense", "contiguous", "masked").index(kind), rows, n, k, 4))
+    names.discard("none")
+    for name in sorted(names):
+        monkeypatch.setenv("DG_FORCE_INSTANCE", name)
+        if kind == "dense":
+            p = I.make_dense(333, 400, 512, seed=5)
+        elif kind == "contiguous":
+            p = I.make_contiguous([256, 128, 384], 400, 384, seed=6)
+        else:
+            p = I.make_masked(3, 200, 400, 384, seed=7, masked_m=[200, 37, 0])
+        check_full(p, f"{kind} forced {name}")
+    monkeypatch.delenv("DG_FORCE_INSTANCE")
+
+
+def test_integer_inputs_bit_exact():
+    rng = np.random.default_rng(40)
+    M, N, K = 200, 300, 384
+    a = np.zeros((M, K))
+    for r in range(M):
+        pos = rng.choice(K, 8, replace=False)
+        a[r, pos] = rng.integers(-4, 5, 8)
+    b = rng.integers(-4, 5, (N, K)).astype(np.float64)
+    ref = (a.astype(np.int64) @ b.astype(np.int64).T).astype(np.float64)
+    p = I.Problem("dense", M, N, K, 1, e4m3_codes_of(a), np.ones((M, 3), np.float32),
+                  e4m3_codes_of(b), np.ones((3, 3), np.float32))
+    gu.say("[case] integer dense")
+    assert np.array_equal(bf16_to_f64(gu.run_gpu(p)), ref)
+    # grouped: a wrong group gives a wrong integer
+    G = 3
+    bs = [rng.integers(-4, 5, (N, K)).astype(np.float64) for _ in range(G)]
+    sizes = [128, 256, 128]
+    ac = a[:512] if a.shape[0] >= 512 else np.concatenate([a, a, a])[:512]
+    gi = I.group_sizes_to_idx(sizes)
+    pc = I.Problem("contiguous", 512, N, K, G, e4m3_codes_of(ac), np.ones((512, 3), np.float32),
+                   e4m3_codes_of(np.concatenate(bs)), np.ones((G * 3, 3), np.float32),
+                   group_idx=gi)
+    gu.say("[case] integer contiguous")
+    got = bf16_to_f64(gu.run_gpu(pc))
+    want = np.concatenate([ac[gi == g].astype(np.int64) @ bs[g].astype(np.int64).T
+                           for g in range(G)]).astype(np.float64)
+    assert np.array_equal(got, want)
+    cap = 160
+    mm = np.array([160, 3, 77], np.int32)
+    am = np.concatenate([a, a, a])[:G * cap]
+    pm = I.Problem("masked", cap, N, K, G, e4m3_codes_of(am), np.ones((G * cap, 3), np.float32),
+                   e4m3_codes_of(np.concatenate(bs)), np.ones((G * 3, 3), np.float32),
+                   masked_m=mm)
+    gu.say("[case] integer masked")
+    got = gu.run_gpu(pm)
+    for g in range(G):
+        blk = got[g * cap:(g + 1) * cap]
+        want = am[g * cap:g * cap + mm[g]].astype(np.int64) @ bs[g].astype(np.int64).T
+        assert np.array_equal(bf16_to_f64(blk[:mm[g]]), want.astype(np.float64))
+        assert np.all(blk[mm[g]:] == SENTINEL)
+
+
+def test_power_of_two_scaling_and_determinism():
+    p = I.make_dense(256, 384, 768, seed=41)
+    gu.say("[case] 2^k scaling")
+    c0 = gu.run_gpu(p)
+    c0b = gu.run_gpu(p)
+    assert np.array_equal(c0, c0b), "two runs differ"
+    sA = p.sA.copy(); sA[7] *= 8.0; sA[200] *= 0.5
+    sB = p.sB.copy(); sB[1] *= 4.0
+    q = I.Problem("dense", p.M, p.N, p.K, 1, p.A, sA, p.B, sB)
+    c1 = bf16_to_f64(gu.run_gpu(q))
+    f0 = bf16_to_f64(c0)
+    f0[7] *= 8.0; f0[200] *= 0.5; f0[:, 128:256] *= 4.0
+    assert np.array_equal(c1, f0)
+
+
+def test_masked_edge_counts_nan_rows_and_sentinel():
+    G, cap, N, K = 6, 96, 300, 512
+    mm = np.array([0, cap, 1, cap - 1, -5, cap + 7], np.int32)
+    p = I.make_masked(G, cap, N, K, seed=42, masked_m=mm)
+    valid = np.clip(mm, 0, cap)
+    A = p.A.copy()
+    for g in range(G):
+        A[g * cap + valid[g]:(g + 1) * cap] = 0x7F       # NaN bytes that must never be read
+    p.A = A
+    check_full(p, "masked edge counts")
+    gu.say("[case] masked all-zero counts")
+    z = gu.run_gpu(p, masked_m=np.zeros(G, np.int32))
+    assert np.all(z == SENTINEL)
+
+
+def test_masked_group_permutation_bit_exact():
+    G, cap, N, K = 4, 128, 256, 384
+    p = I.make_masked(G, cap, N, K, seed=43, masked_m=[128, 50, 0, 77])
+    c = gu.run_gpu(p)
+    perm = [2, 0, 3, 1]
+    nnb = 2
+    ra = np.concatenate([np.arange(g * cap, (g + 1) * cap) for g in perm])
+    rb = np.concatenate([np.arange(g * N, (g + 1) * N) for g in perm])
+    rs = np.concatenate([np.arange(g * nnb, (g + 1) * nnb) for g in perm])
+    q = I.Problem("masked", cap, N, K, G, p.A[ra], p.sA[ra], p.B[rb], p.sB[rs],
+                  masked_m=p.masked_m[perm])
+    gu.say("[case] masked permutation")
+    assert np.array_equal(gu.run_gpu(q), c[ra])
+
+
+def test_contiguous_malformed_rows_and_permutation():
+    sizes = [256, 128, 384, 128]
+    p = I.make_contiguous(sizes, 300, 384, seed=44)
+    gi = p.group_idx.copy()
+    gi[250:256] = -1
+    gi[300] = 0
+    gi[130] = 9
+    gi[640:768] = -1
+    check_full(p, "contiguous malformed rows", group_idx=gi)
+    c = gu.run_gpu(p)
+    starts = np.cumsum([0] + sizes)
+    order = [3, 1, 0, 2]
+    rows = np.concatenate([np.arange(starts[g], starts[g + 1]) for g in order])
+    q = I.Problem("contiguous", p.rows, p.N, p.K, p.G, p.A[rows], p.sA[rows], p.B, p.sB,
+                  group_idx=p.group_idx[rows])
+    gu.say("[case] contiguous permutation")
+    assert np.array_equal(gu.run_gpu(q), c[rows])
+
+
+def test_contiguous_single_group_matches_dense():
+    p = I.make_contiguous([512], 384, 512, seed=45)
+    d = I.Problem("dense", 512, 384, 512, 1, p.A, p.sA, p.B, p.sB)
+    c1 = gu.run_gpu(p)
+    c2 = gu.run_gpu(d)
+    assert_within_tolerance(c1, c2, np.ones_like(c1, bool), "contiguous G=1 vs dense")
+
+
+def test_empty_calls_are_noops():
+    from moe_grouped_gemm_lhs_amd import binding as b
+    A = torch.zeros((0, 128), dtype=torch.uint8, device=gu.DEV)
+    sA = torch.zeros((0, 1), dtype=torch.float32, device=gu.DEV)
+    B = torch.zeros((16, 128), dtype=torch.uint8, device=gu.DEV)
+    sB = torch.ones((1, 1), dtype=torch.float32, device=gu.DEV)
+    C = b.dg_gemm_fp8_nt(A, sA, B, sB)
+    assert C.shape == (0, 16)
+
+
+# ------------------------------------------------------------- the workload shapes
+@pytest.mark.parametrize("case", I.decode_cases(), ids=I.case_name)
+def test_decode_shapes_full(case):
+    p = I.make(case)
+    check_full(p, I.case_name(case))
+
+
+@pytest.mark.parametrize("case", I.prefill_cases(), ids=I.case_name)
+def test_prefill_shapes_sampled(case):
+    p = I.make(case)
+    check_sampled(p, I.case_name(case))
+
+
+@pytest.mark.parametrize("case", I.contiguous_cases(), ids=I.case_name)
+def test_contiguous_shapes_sampled(case):
+    p = I.make(case)
+    check_sampled(p, I.case_name(case))
+
+
+@pytest.mark.parametrize("case", I.masked_cases(), ids=I.case_name)
+def test_masked_shapes_sampled(case):
+    p = I.make(case)
+    check_sampled(p, I.case_name(case) + f" masked_m={p.masked_m.tolist()}")
