@@ -34,6 +34,7 @@ def parse():
                     choices=["decode", "prefill", "contiguous", "masked", "small"])
     ap.add_argument("--shapes", default="", help="comma-separated subset of shape indices")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches, not a graph")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--detail", default="", help="write per-shape details to this JSON file")
     return ap.parse_args()
@@ -95,6 +96,14 @@ def main():
     # ---- inputs: generated on the host, made resident in HBM before timing
     t0 = time.time()
     problems, calls = [], []
+    # one workspace, zero filled once, shared by every call in stream order
+    ws_need = 0
+    for case in cases:
+        kind_id = {"dense": 0, "contiguous": 1, "masked": 2}[case["kind"]]
+        rows = case.get("M") or case.get("cap") or sum(case.get("sizes", [0]))
+        ws_need = max(ws_need, dg.dg_workspace_bytes(kind_id, rows, case["N"], case["K"],
+                                                     case.get("G", len(case.get("sizes", [1])))))
+    ws = torch.zeros(max(ws_need, 16), dtype=torch.uint8, device=dev)
     for case in cases:
         p = I.make(case)
         nkb, nnb = p.K // 128, -(-p.N // 128)
@@ -105,20 +114,20 @@ def main():
         if p.kind == "dense":
             B, sB = B.view(p.N, p.K), sB.view(nnb, nkb)
             C = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
-            fn = (lambda A=A, sA=sA, B=B, sB=sB, C=C: dg.dg_gemm_fp8_nt(A, sA, B, sB, C))
+            fn = (lambda A=A, sA=sA, B=B, sB=sB, C=C: dg.dg_gemm_fp8_nt(A, sA, B, sB, C, workspace=ws))
         elif p.kind == "contiguous":
             B, sB = B.view(p.G, p.N, p.K), sB.view(p.G, nnb, nkb)
             gi = torch.from_numpy(p.group_idx).to(dev)
             C = torch.empty((p.rows, p.N), dtype=torch.bfloat16, device=dev)
             fn = (lambda A=A, sA=sA, B=B, sB=sB, gi=gi, C=C:
-                  dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, gi, C))
+                  dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, gi, C, workspace=ws))
         else:
             A, sA = A.view(p.G, p.M, p.K), sA.view(p.G, p.M, nkb)
             B, sB = B.view(p.G, p.N, p.K), sB.view(p.G, nnb, nkb)
             mm = torch.from_numpy(p.masked_m).to(dev)
             C = torch.empty((p.G, p.M, p.N), dtype=torch.bfloat16, device=dev)
             fn = (lambda A=A, sA=sA, B=B, sB=sB, mm=mm, C=C:
-                  dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, mm, C))
+                  dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, mm, C, workspace=ws))
         flops, nbytes = work_of(p)
         kind_id = {"dense": 0, "contiguous": 1, "masked": 2}[p.kind]
         inst = dg.dg_instance_name(kind_id, p.M if p.kind != "contiguous" else p.rows, p.N, p.K, p.G)
@@ -136,20 +145,53 @@ def main():
             c["fn"]()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps; HIP events around every launch on the launch stream
+    # ---- the step as one HIP graph (the calls read their routing from device memory and
+    # never synchronise, so a captured step replays exactly); eager launches otherwise
+    graph = None
+    if not args.no_graph:
+        try:
+            cap = torch.cuda.Stream(dev)
+            cap.wait_stream(stream)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=cap):
+                for c in calls:
+                    c["fn"]()
+            torch.cuda.synchronize()
+            for _ in range(max(1, args.warmup)):
+                graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # pragma: no cover - fall back to eager steps
+            print(f"[bench] graph capture unavailable ({e}); timing eager steps", file=sys.stderr)
+            graph = None
+
+    def one_step():
+        if graph is not None:
+            graph.replay()
+        else:
+            for c in calls:
+                c["fn"]()
+
+    # ---- timed region 1: K whole steps (the job's throughput)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        one_step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    wall_s = t_end - t_start
+    ms_per_step = wall_s * 1e3 / args.steps
+
+    # ---- timed region 2: K eager steps with HIP events around every launch, recorded on
+    # the stream the kernels run on (per-shape durations; the roofline's kernel time)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in calls] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t_start = time.perf_counter()
     for s in range(args.steps):
         for i, c in enumerate(calls):
             ev[s][i][0].record(stream)
             c["fn"]()
             ev[s][i][1].record(stream)
     torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    wall_s = t_end - t_start
-    ms_per_step = wall_s * 1e3 / args.steps
 
     per = []
     for i, c in enumerate(calls):
@@ -193,7 +235,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
         "data": "synthetic (seeded N(0,1), 1x128 / 128x128 e4m3fn block quantisation)",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "shapes": len(calls),
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "step": "one HIP graph of all shapes" if graph is not None else "eager launches"},
         "tflops": round(total_flops / step_s / 1e12, 2),
         "gbs": round(total_bytes / step_s / 1e9, 1),
         "roofline": roof,

@@ -242,3 +242,47 @@ def test_contiguous_shapes_sampled(case):
 def test_masked_shapes_sampled(case):
     p = I.make(case)
     check_sampled(p, I.case_name(case) + f" masked_m={p.masked_m.tolist()}")
+
+
+def test_graph_capture_replays_with_new_counts():
+    """The masked call (and a stream-K decode call that uses the workspace counters)
+    captured once in a HIP graph and replayed with new masked_m values written between
+    replays: every replay matches the oracle, rows past the counts stay untouched."""
+    from moe_grouped_gemm_lhs_amd import binding as dg
+    G, cap, N, K = 3, 128, 512, 1024
+    p = I.make_masked(G, cap, N, K, seed=46, masked_m=[128, 40, 0])
+    A, sA, B, sB = gu.device_operands(p)
+    mm = torch.tensor([128, 40, 0], dtype=torch.int32, device=gu.DEV)
+    C = torch.empty((G, cap, N), dtype=torch.bfloat16, device=gu.DEV)
+    d = I.make_dense(64, 2112, 1024, seed=47)
+    dA, dsA, dB, dsB = gu.device_operands(d)
+    dC = torch.empty((64, 2112), dtype=torch.bfloat16, device=gu.DEV)
+    ws = torch.zeros(dg.dg_workspace_bytes(0, 64, 2112, 1024, 1) + 16, dtype=torch.uint8,
+                     device=gu.DEV)
+    sentinel = int(np.uint16(SENTINEL).view(np.int16))
+    gu.say("[case] graph capture")
+    dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, mm, C)
+    dg.dg_gemm_fp8_nt(dA, dsA, dB, dsB, dC, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, mm, C)
+        dg.dg_gemm_fp8_nt(dA, dsA, dB, dsB, dC, workspace=ws)
+    torch.cuda.synchronize()
+    ref_dense = gu.oracle_full(d)
+    for counts in ([128, 40, 0], [5, 128, 77], [0, 0, 1], [128, 128, 128]):
+        gu.say(f"[case] graph replay masked_m={counts}")
+        mm.copy_(torch.tensor(counts, dtype=torch.int32))
+        C.view(torch.int16).fill_(sentinel)
+        dC.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = C.view(torch.int16).cpu().numpy().view(np.uint16).reshape(G * cap, N)
+        ref = gu.oracle_full(p, masked_m=np.array(counts, np.int32))
+        w = np.repeat(gu.written_rows(p, masked_m=np.array(counts))[:, None], N, axis=1)
+        assert_within_tolerance(got, ref, w, f"graph replay {counts}")
+        got_d = dC.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert_within_tolerance(got_d, ref_dense, np.ones_like(got_d, bool), "graph replay dense")
