@@ -183,10 +183,14 @@ def main():
 
     # ---- timed region 2: K eager steps with HIP events around every launch, recorded on
     # the stream the kernels run on (per-shape durations; the roofline's kernel time)
+    # Each step's launches are queued behind a short device-side spin, so that the host
+    # runs ahead and the events bracket the kernels alone, not the host's launch latency.
+    spin = _spin_cycles_for(torch, stream, 40e-6 * len(calls) + 50e-6)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in calls] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for s in range(args.steps):
+        torch.cuda._sleep(spin)
         for i, c in enumerate(calls):
             ev[s][i][0].record(stream)
             c["fn"]()
@@ -249,45 +253,64 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(problems, calls, budget_s, hbm_bound):
-    """Time the CPU oracle on a bounded sample of the workload: whole shapes in order
-    while the budget lasts, else the leading rows of a shape; throughput is scaled to
-    the metric's unit from the work actually done."""
+def _spin_cycles_for(torch, stream, seconds):
+    """Cycle count for torch.cuda._sleep that keeps the device busy for about `seconds`."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    probe = 1 << 20
+    torch.cuda._sleep(probe)            # first call loads the spin kernel
+    torch.cuda.synchronize()
+    e0.record(stream)
+    torch.cuda._sleep(probe)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per_cycle_s = max(e0.elapsed_time(e1) * 1e-3 / probe, 1e-12)
+    return int(min(seconds / per_cycle_s, 1 << 40))
+
+
+def cpu_baseline(problems, calls, budget_s, hbm_bound, min_s=10.0):
+    """Time the CPU oracle on a bounded sample of the workload: whole shapes in order,
+    repeated until at least min_s of oracle time has been spent, and the leading rows of
+    a shape when a whole one would overrun budget_s; throughput is scaled to the
+    metric's unit from the work actually done."""
     import oracle
     from moe_grouped_gemm_lhs_amd import accounting as acc
 
-    done_s, done_flops, done_bytes, parts = 0.0, 0, 0, []
-    for p, c in zip(problems, calls):
-        if done_s >= budget_s:
-            break
-        if p.kind != "dense":
-            rows = p.rows if p.kind == "contiguous" else p.G * p.M
-        else:
-            rows = p.M
-        # estimate from one small slice first: never overrun the budget by much
-        r_probe = min(rows, max(1, oracle.threads()))
-        t = time.perf_counter()
-        _oracle_rows(p, r_probe)
-        dt = time.perf_counter() - t
-        per_row = dt / r_probe
-        r = int(min(rows, max(r_probe, (budget_s - done_s - dt) / max(per_row, 1e-9))))
-        if r > r_probe:
+    done_s, done_flops, done_bytes = 0.0, 0, 0
+    parts = {}
+    passes = 0
+    while done_s < min_s and done_s < budget_s:
+        passes += 1
+        for p, c in zip(problems, calls):
+            if done_s >= budget_s:
+                break
+            if p.kind != "dense":
+                rows = p.rows if p.kind == "contiguous" else p.G * p.M
+            else:
+                rows = p.M
+            # estimate from one small slice first: never overrun the budget by much
+            r_probe = min(rows, max(1, oracle.threads()))
             t = time.perf_counter()
-            _oracle_rows(p, r)
+            _oracle_rows(p, r_probe)
             dt = time.perf_counter() - t
-        else:
-            r = r_probe
-        done_s += dt
-        f, b = acc.flops(r, p.N, p.K), acc.algorithmic_bytes(r, p.N, p.K, 1)
-        done_flops += f
-        done_bytes += b
-        parts.append(f"{c['name']}:{r}/{rows} rows")
+            per_row = dt / r_probe
+            r = int(min(rows, max(r_probe, (budget_s - done_s - dt) / max(per_row, 1e-9))))
+            if r > r_probe:
+                t = time.perf_counter()
+                _oracle_rows(p, r)
+                dt = time.perf_counter() - t
+            else:
+                r = r_probe
+            done_s += dt
+            done_flops += acc.flops(r, p.N, p.K)
+            done_bytes += acc.algorithmic_bytes(r, p.N, p.K, 1)
+            parts[c["name"]] = f"{c['name']}:{r}/{rows} rows"
     if hbm_bound:
         value, unit = done_bytes / done_s / 1e9, "GB/s"
     else:
         value, unit = done_flops / done_s / 1e12, "TFLOP/s"
     return {"value": round(value, 4), "unit": unit, "cores": oracle.threads(), "kind": "oracle",
-            "sample": "; ".join(parts) + f" ({done_s:.1f} s of oracle time)",
+            "sample": f"{passes} pass(es) over " + "; ".join(parts.values())
+                      + f" ({done_s:.1f} s of oracle time)",
             "tflops": round(done_flops / done_s / 1e12, 5)}
 
 
