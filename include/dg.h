@@ -47,10 +47,10 @@
  *     captured in a HIP graph.  Faults inside kernels surface at the caller's next
  *     synchronisation.  Results are deterministic: the same inputs give the same bits.
  *   - Workspace: device memory the caller lends for split-K partial sums, at least
- *     dg_workspace_bytes(...) bytes, 16-byte aligned.  Its first 64 KiB hold arrival
- *     counters that must be zero before the first use; every call leaves them zero
- *     again, so one workspace can serve calls of any shape in stream order.  Two calls
- *     that may run concurrently must not share one workspace.
+ *     dg_workspace_bytes(...) bytes, 16-byte aligned.  It must be zero filled before
+ *     its first use; every call leaves it zero filled again (a zero word marks a partial
+ *     not yet written), so one workspace can serve calls of any shape in stream order.
+ *     Two calls that may run concurrently must not share one workspace.
  */
 #ifndef DG_H_
 #define DG_H_

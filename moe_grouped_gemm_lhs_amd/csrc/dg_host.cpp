@@ -99,7 +99,7 @@ double tile_cost(int64_t rows, int64_t N, int64_t groups, int bm, int bn, double
 // (column tile, wave).
 bool stream_fits(const Instance* in, int64_t rows, int64_t N) {
   if (in->mode == dg::kModeStream)
-    return rows <= in->bm && cdiv(N, in->bn) * (in->threads / 64) <= dg::kCounterSlots;
+    return rows <= in->bm;
   return true;
 }
 
@@ -117,8 +117,8 @@ const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_
   switch (kind) {
     case dg::kDense:
       // decode-shaped (all rows in one tile): persistent stream-K over the column tiles
-      // and K blocks, as long as the per-wave arrival counters fit their header
-      if (rows_or_cap <= 128 && cdiv(N, 64) * 4 <= dg::kCounterSlots) {
+      // and K blocks
+      if (rows_or_cap <= 128) {
         // 128-column tiles when every CU gets long runs of K blocks; 64-column tiles
         // otherwise (fewer contributors per shared tile)
         const int64_t tiles128 = cdiv(N, 128), nkb = K / dg::kBlockK;
@@ -166,8 +166,8 @@ void fill_tiles(GemmArgs& a, const Instance* in, int kind) {
 
 size_t workspace_for(const Instance* in, const GemmArgs& a) {
   if (!in) return 0;
-  if (in->mode == dg::kModeStream)   // counter header + two partial tiles per workgroup
-    return dg::kCounterBytes + (size_t)dg::kStreamGrid * 2 * in->bm * in->bn * sizeof(float);
+  if (in->mode == dg::kModeStream)   // two partial tiles per workgroup
+    return (size_t)dg::kStreamGrid * 2 * in->bm * in->bn * sizeof(float);
   return 0;
 }
 
@@ -178,10 +178,9 @@ dg_status run(int kind, GemmArgs& a, void* workspace, size_t workspace_bytes, vo
   const size_t ws = workspace_for(in, a);
   if (ws > 0) {
     if (!workspace || workspace_bytes < ws || !aligned(workspace, 16)) return DG_ERR_WORKSPACE;
-    a.counters = (uint32_t*)workspace;
-    a.partial = (float*)((char*)workspace + dg::kCounterBytes);
+    a.partial = (float*)workspace;
   }
-  if (in->mode == dg::kModeStream && (!a.partial || !a.counters))
+  if (in->mode == dg::kModeStream && !a.partial)
     return DG_ERR_WORKSPACE;
   int num_cus = 0;
   dg_status st = check_device(&num_cus);

@@ -10,18 +10,19 @@ namespace dg {
 
 constexpr int kBlockK = 128;       // depth of one scaled K block
 constexpr int kAlignM = 128;       // contiguous-layout row alignment
-// Stream-K workspace layout: arrival counters in a fixed header at offset 0 (every call
-// leaves them zero, whatever its shape), fp32 partial tiles after it.
-constexpr int kCounterSlots = 16384;
-// Stream-K instances run at most this many workgroups (their workspace holds two
-// partial tiles per workgroup).
+// Stream-K workspace: two fp32 partial tiles per workgroup, stored bit-inverted (zero
+// means "not written"); it must be zero filled before the first call, and every call
+// leaves it zero filled.
+// Stream-K instances run at most this many workgroups.
 constexpr int kStreamGrid = 256;
+// Bound on a contributor's wait for the other partials of its tile: polls of about
+// 0.1-2 us each, so well under a second; a legitimate wait is a few microseconds.  A
+// fragment whose wait runs out is stored as NaN.
+constexpr int kSpinLimit = 1 << 16;
 
 // Instance modes.
 constexpr int kModeTiled = 0;    // one output tile per work item
 constexpr int kModeStream = 2;   // persistent stream-K over (tile, K block) iterations
-
-constexpr size_t kCounterBytes = kCounterSlots * sizeof(uint32_t);
 
 enum Kind : int { kDense = 0, kContiguous = 1, kMasked = 2 };
 
@@ -35,7 +36,6 @@ struct GemmArgs {
   const int32_t* group_idx;   // contiguous only
   const int32_t* masked_m;    // masked only
   float* partial;             // stream-K fp32 partial tiles (workspace), or nullptr
-  uint32_t* counters;         // stream-K arrival counters (workspace), or nullptr
   int rows;                   // dense M, contiguous M_total, masked cap
   int N, K, G;
   int nkb;                    // K / 128

@@ -71,8 +71,11 @@ __device__ __forceinline__ void wait_stages_ahead(int ahead) {
   }
 }
 
+// 16 bytes per lane; AUX is the cache policy (0: default, 2: non-temporal, for operands
+// that are read once and would only evict reused data from the caches).
+template <int AUX = 0>
 __device__ __forceinline__ void dma16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, AUX);
 }
 __device__ __forceinline__ void dma4(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 4, 0, 0);
@@ -86,6 +89,17 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Split-K partials are stored bit-inverted, so that an all-zero word marks a slot not
+// yet written.  The only value whose inverse is zero, the NaN with every bit set, is
+// first replaced by another NaN.
+__device__ __forceinline__ v4i encode_partial(v4f v) {
+  v4i u = __builtin_bit_cast(v4i, v);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) u[e] = ~(u[e] == -1 ? (int)0xFFC00000u : u[e]);
+  return u;
+}
+__device__ __forceinline__ v4f decode_partial(v4i u) { return __builtin_bit_cast(v4f, ~u); }
 
 __device__ __forceinline__ v8i read_frag(const uint8_t* base, int row, int q) {
   const uint8_t* r = base + row * kBlockK;
@@ -106,10 +120,13 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 // Compile-time shape of one kernel instance.
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_>
+// B_NT: B blocks are read by exactly one workgroup (decode shapes), so they are loaded
+// non-temporal.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, bool B_NT_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int STAGES = STAGES_;
+  static constexpr bool B_NT = B_NT_;
   static constexpr int W = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * W;
   static constexpr int WM = BM / WAVES_M;       // rows per wave
@@ -228,7 +245,8 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
   for (int it = 0; it < C::B_DMA; ++it) {
     const int cb = c.wave * C::B_DMA + it;
     const int n = min(c.n0 + cb * 8 + sub, c.N - 1);
-    dma16(c.Bg + (size_t)n * c.K + kb * kBlockK + ch * 16, st + C::A_BYTES + cb * 1024);
+    dma16<C::B_NT ? 2 : 0>(c.Bg + (size_t)n * c.K + kb * kBlockK + ch * 16,
+                           st + C::A_BYTES + cb * 1024);
   }
   const int s = c.wave * 64 + c.lane;
   const float* src;
@@ -458,12 +476,19 @@ gemm_fp8_kernel(GemmArgs p) {
 // persistent grid, so every CU streams the same share of B whatever the shape, and one
 // load pipeline runs through a workgroup's whole range, across tile boundaries.
 // A tile whose K blocks all fall in one workgroup's range is stored as bf16 directly.
-// A tile shared by several workgroups is reduced deterministically: each contributor
-// writes its fp32 partial (per wave, in fragment order: one contiguous 1 KB block per
-// 16x16 sub-tile) with device-coherent (sc1) stores; after its loop, with every store
-// complete, it bumps the tile's per-wave arrival counter; the wave that arrives last
-// adds the contributors' partials in workgroup order and stores bf16.  A workgroup
-// holds at most two shared tiles: the first and the last of its range.
+// A tile shared by n workgroups (its contributors, consecutive in workgroup order) is
+// reduced deterministically and in parallel, with no atomics: each contributor writes its
+// fp32 partial in fragment order (one contiguous 1 KB block per 16x16 sub-tile) with
+// device-coherent (sc1) stores, every value stored bit-inverted so that a zero word
+// means "not written yet" (the workspace starts zero filled).  After its loop, each
+// contributor reduces every n-th fragment of the tile (its own share): it polls each
+// contributor's slot until all of its words are non-zero, sums the contributors in
+// workgroup order, stores those fragments as bf16 and writes zeros back, which leaves
+// the workspace zero filled for the next call.  Every workgroup writes all its partials
+// before it waits on any, and the persistent grid never exceeds the CU count with one
+// workgroup per CU (the LDS budget admits no second), so all contributors are resident
+// and every wait ends; the wait is bounded all the same.  A workgroup holds at most two
+// shared tiles: the first and the last of its range.
 template <class C>
 __device__ __forceinline__ long stream_start(long g, long W, long G) { return g * W / G; }
 
@@ -562,7 +587,7 @@ gemm_fp8_stream_kernel(GemmArgs p) {
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          __builtin_amdgcn_raw_buffer_store_b128(acc[i][j], part_rsrc,
+          __builtin_amdgcn_raw_buffer_store_b128(encode_partial(acc[i][j]), part_rsrc,
                                                  base + ((i * TJ + j) * 64 + lane) * 16, 0,
                                                  16 /* sc1: device coherent */);
     }
@@ -574,53 +599,103 @@ gemm_fp8_stream_kernel(GemmArgs p) {
     in_tile = 0;
   }
 
-  // hand-off of the shared tiles: all partial stores of this workgroup are complete
-  wait_vmcnt<0>();
-#pragma unroll
+  // ---- reduction of the shared tiles: this workgroup's share of each.  Wave w takes
+  // the share's fragments w, w + W, ... two at a time; for each pair it fetches the
+  // contributors' 1 KB slots CB at a time with all loads in flight together (polled
+  // until written), sums them in workgroup order, zeroes the slots, and stores bf16.
+  // Waves work independently: no barrier.
+  constexpr int F = C::W * TI * TJ;                        // fragments per tile
+  constexpr int CB = 8;                                    // contributors per fetch
+  constexpr int kPastBuffer = 0x7FFFFF00;                  // beyond part_rsrc's range
+#pragma unroll 1
   for (int seg = 0; seg < 2; ++seg) {
     const int t = shared_tile[seg];
     if (t < 0) continue;
-    uint32_t* ctr = p.counters + (size_t)t * C::W + wave;
-    unsigned old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = (unsigned)__builtin_amdgcn_readfirstlane((int)old);
-    // contributors: the workgroups whose ranges meet iterations [t*nkb, (t+1)*nkb)
     const long x0 = (long)t * nkb, x1 = x0 + nkb - 1;
     const long g_first = ((x0 + 1) * G + W - 1) / W - 1;
     const long g_last = ((x1 + 1) * G + W - 1) / W - 1;
-    if (old != (unsigned)(g_last - g_first)) continue;   // not the last to arrive
-    v4f sum[TI][TJ];
+    const int n = (int)(g_last - g_first + 1);
+    const int me = (int)(g - g_first);
+    const int fm = me < F ? (F - me + n - 1) / n : 0;     // fragments me, me+n, ...
+#pragma unroll 1
+    for (int k = wave; k < fm; k += 2 * C::W) {
+      const bool two = k + C::W < fm;
+      const int f0 = me + n * k, f1 = me + n * (k + C::W);
+      v4f sum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 1
+      for (int c0 = 0; c0 < n; c0 += CB) {
+        // slot offsets; unused ones lie beyond the buffer's range, where the buffer load
+        // returns zeros without touching memory, so every load is unconditional
+        int off[2][CB];
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+        for (int u = 0; u < CB; ++u) {
+          const long gg = g_first + c0 + u;
+          const bool live = c0 + u < n;
+          // slot 0 if gg's range starts inside tile t (gg*W/G >= t*nkb), else slot 1
+          const int sg = gg * W >= x0 * G ? 0 : 1;
+          const long base = (gg * 2 + sg) * F;
+          off[0][u] = live ? (int)(((base + f0) * 64 + lane) * 16) : kPastBuffer;
+          off[1][u] = live && two ? (int)(((base + f1) * 64 + lane) * 16) : kPastBuffer;
+        }
+        v4i raw[2][CB];
+        bool ready = false;
+#pragma unroll 1
+        for (int spin = 0; spin < kSpinLimit && !ready; ++spin) {
+          if (spin > 0) __builtin_amdgcn_s_sleep(2);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) sum[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-    // contributors in workgroup order, RB at a time so that their loads overlap
-    constexpr int RB = TI * TJ <= 8 ? 4 : 2;
-    for (long g0 = g_first; g0 <= g_last; g0 += RB) {
-      v4f part[RB][TI][TJ];
+          for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int u = 0; u < RB; ++u) {
-        const long gg = min(g0 + u, g_last);
-        const int sg = (int)(stream_start<C>(gg, W, G) / nkb) == t ? 0 : 1;
-        const int base = (int)(((gg * 2 + sg) * C::W + wave) * WAVE_SLOT) * 4;
+            for (int u = 0; u < CB; ++u)
+              raw[r][u] = __builtin_amdgcn_raw_buffer_load_b128(part_rsrc, off[r][u], 0,
+                                                                16 /* sc1 */);
+          bool mine = true;
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+          for (int r = 0; r < 2; ++r)
 #pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            part[u][i][j] = __builtin_amdgcn_raw_buffer_load_b128(
-                part_rsrc, base + ((i * TJ + j) * 64 + lane) * 16, 0, 16 /* sc1 */);
+            for (int u = 0; u < CB; ++u) {
+              const bool ok = raw[r][u].x != 0 && raw[r][u].y != 0 && raw[r][u].z != 0 &&
+                              raw[r][u].w != 0;
+              mine = mine && (ok || off[r][u] == kPastBuffer);
+            }
+          ready = __builtin_amdgcn_ballot_w64(!mine) == 0;
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int u = 0; u < CB; ++u) {
+            if (off[r][u] == kPastBuffer) continue;
+            // a wait that ran out leaves the fragment NaN
+            sum[r] += ready ? decode_partial(raw[r][u])
+                            : (v4f){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                    __builtin_nanf("")};
+            __builtin_amdgcn_raw_buffer_store_b128((v4i){0, 0, 0, 0}, part_rsrc, off[r][u], 0,
+                                                   16 /* sc1 */);
+          }
       }
 #pragma unroll
-      for (int u = 0; u < RB; ++u)
-        if (g0 + u <= g_last) {
+      for (int r = 0; r < 2; ++r) {
+        if (r == 1 && !two) break;
+        const int f = r == 0 ? f0 : f1;
+        const v4f v = sum[r];
+        const int sw = f / (TI * TJ), rem = f - sw * (TI * TJ);
+        const int fi = rem / TJ, fj = rem - fi * TJ;
+        const int swm = sw / C::WAVES_N, swn = sw - swm * C::WAVES_N;
+        const int row = swm * C::WM + 16 * fi + l16;
+        const int col = t * C::BN + swn * C::WN + 16 * fj + 4 * q;
+        if (row < p.rows) {
+          uint16_t* dst = p.C + (size_t)row * p.N;
+          if (((p.N & 3) == 0) && col + 3 < p.N) {
+            const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+            const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+            *(uint2*)(dst + col) = make_uint2(lo, hi);
+          } else {
 #pragma unroll
-          for (int i = 0; i < TI; ++i)
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) sum[i][j] += part[u][i][j];
+            for (int e = 0; e < 4; ++e)
+              if (col + e < p.N) dst[col + e] = (uint16_t)bf16_rne_bits(v[e]);
+          }
         }
+      }
     }
-    store_tile_bf16<C>(sum, p.C, p.N, 0, p.rows, t * C::BN, wm, wn, q, l16);
-    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -651,10 +726,12 @@ using Big = Cfg<256, 256, 4, 2, 2>;      // 8 waves, 64x128 per wave
 using Big224 = Cfg<256, 224, 4, 2, 2>;   // non-power-of-two columns: 64x112 per wave
 using Mid = Cfg<128, 128, 2, 2, 3>;      // 4 waves, 64x64 per wave
 using Small = Cfg<64, 128, 1, 4, 4>;     // 4 waves, 64x32 per wave, 4 stages
-using Str64 = Cfg<64, 128, 1, 4, 5>;     // stream-K decode: 64 rows x 128 columns
-using Str64n64 = Cfg<64, 64, 1, 4, 8>;   // stream-K decode: 64 rows x 64 columns
-using Str128 = Cfg<128, 128, 1, 4, 4>;   // stream-K decode: 128 rows x 128 columns
-using Str128n64 = Cfg<128, 64, 1, 4, 6>; // stream-K decode: 128 rows x 64 columns
+// stream-K decode instances: 8 waves (a wave's direct-to-LDS copies are issue-bound, so
+// a workgroup needs eight of them to draw its share of HBM bandwidth), B non-temporal
+using Str64 = Cfg<64, 128, 2, 4, 5, true>;     // 64 rows x 128 columns
+using Str64n64 = Cfg<64, 64, 2, 4, 8, true>;   // 64 rows x 64 columns
+using Str128 = Cfg<128, 128, 2, 4, 4, true>;   // 128 rows x 128 columns
+using Str128n64 = Cfg<128, 64, 2, 4, 6, true>; // 128 rows x 64 columns
 
 }  // namespace
 

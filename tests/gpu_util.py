@@ -39,14 +39,14 @@ def out_shape(p):
     return (p.rows, p.N)
 
 
-def run_gpu(p, c_init_bits=None, group_idx=None, masked_m=None, ops=None):
+def run_gpu(p, c_init_bits=None, group_idx=None, masked_m=None, ops=None, workspace=None):
     """Run the problem on the GPU; returns C as uint16 bits (rows x N)."""
     A, sA, B, sB = ops if ops is not None else device_operands(p)
     if c_init_bits is None:
         c_init_bits = np.full(out_shape(p), SENTINEL, np.uint16)
     C = torch.from_numpy(c_init_bits.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
     if p.kind == "dense":
-        dg.dg_gemm_fp8_nt(A, sA, B, sB, C)
+        dg.dg_gemm_fp8_nt(A, sA, B, sB, C, workspace=workspace)
     elif p.kind == "contiguous":
         gi = group_idx if group_idx is not None else p.group_idx
         dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, torch.from_numpy(gi).to(DEV), C)

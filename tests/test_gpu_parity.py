@@ -95,6 +95,36 @@ def test_every_instance_on_ragged_problem(kind, monkeypatch):
     monkeypatch.delenv("DG_FORCE_INSTANCE")
 
 
+STREAM_INSTANCES = ["dense_64x64_stream", "dense_64x128_stream", "dense_128x64_stream",
+                    "dense_128x128_stream"]
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 128 * 200), (128, 200, 16384), (1, 130, 128 * 64),
+                                   (100, 1000, 128 * 40), (128, 4100, 1024), (37, 640, 128)])
+def test_stream_k_shared_tiles(M, N, K, monkeypatch):
+    """Split-K decode instances: tiles shared by up to ~200 workgroups (one 64-column tile
+    over 200 K blocks), ragged N, a single row, every stream instance that fits the rows;
+    the workspace must be zero filled again after every call."""
+    from moe_grouped_gemm_lhs_amd import binding as b
+    p = I.make_dense(M, N, K, seed=M + N + K // 128)
+    A, sA, B, sB = gu.device_operands(p)
+    c_ref = gu.oracle_full(p)
+    written = np.ones((M, N), bool)
+    for name in STREAM_INSTANCES:
+        if M > int(name.split("_")[1].split("x")[0]):
+            continue
+        monkeypatch.setenv("DG_FORCE_INSTANCE", name)
+        assert b.dg_instance_name(0, M, N, K, 1) == name
+        need = b.dg_workspace_bytes(0, M, N, K, 1)
+        ws = torch.zeros(need, dtype=torch.uint8, device=gu.DEV)
+        for rep in range(2):     # the second call reuses the workspace the first left
+            gu.say(f"[case] stream {name} {M}x{N}x{K} call {rep}")
+            c_gpu = gu.run_gpu(p, ops=(A, sA, B, sB), workspace=ws)
+            assert_within_tolerance(c_gpu, c_ref, written, f"{name} {M}x{N}x{K}")
+            assert not ws.cpu().numpy().any(), f"{name}: workspace not left zero filled"
+    monkeypatch.delenv("DG_FORCE_INSTANCE")
+
+
 def test_integer_inputs_bit_exact():
     rng = np.random.default_rng(40)
     M, N, K = 200, 300, 384
@@ -245,7 +275,7 @@ def test_masked_shapes_sampled(case):
 
 
 def test_graph_capture_replays_with_new_counts():
-    """The masked call (and a stream-K decode call that uses the workspace counters)
+    """The masked call (and a stream-K decode call that uses the workspace)
     captured once in a HIP graph and replayed with new masked_m values written between
     replays: every replay matches the oracle, rows past the counts stay untouched."""
     from moe_grouped_gemm_lhs_amd import binding as dg
