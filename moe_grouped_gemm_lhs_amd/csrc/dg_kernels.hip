@@ -71,6 +71,16 @@ __device__ __forceinline__ void wait_stages_ahead(int ahead) {
   }
 }
 
+// The same for a kernel instance's copies: PER_STAGE per stage for the waves that also
+// copy scales, PER_N for the others (`wave` is uniform).
+template <class C, int A>
+__device__ __forceinline__ void wait_stage_copies(int wave, int ahead) {
+  if (wave < C::S_WAVES)
+    wait_stages_ahead<C::PER_STAGE, A>(ahead);
+  else
+    wait_stages_ahead<C::PER_N, A>(ahead);
+}
+
 // 16 bytes per lane; AUX is the cache policy (0: default, 2: non-temporal, for operands
 // that are read once and would only evict reused data from the caches).
 template <int AUX = 0>
@@ -139,16 +149,22 @@ struct Cfg {
   static constexpr int B_DMA = (BN / 8 + W - 1) / W;
   static constexpr int A_BYTES = A_DMA * W * 8 * kBlockK;
   static constexpr int B_BYTES = B_DMA * W * 8 * kBlockK;
-  static constexpr int S_FLOATS = 64 * W;       // sA for BM rows, then the tile's sB values
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + 4 * S_FLOATS;
-  static constexpr int PER_STAGE = A_DMA + B_DMA + 1;
   static constexpr int NBV = (BN + 127) / 128 + 1;   // sB blocks a tile can touch
+  // scale slots: sA for BM rows, then the tile's sB values; only the first S_WAVES
+  // waves copy them (one 4-byte-per-lane copy each per stage)
+  static constexpr int S_WAVES = (BM + NBV + 63) / 64;
+  static constexpr int S_FLOATS = 64 * S_WAVES;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + 4 * S_FLOATS;
+  // copies per stage of a wave without / with a scale copy
+  static constexpr int PER_N = A_DMA + B_DMA;
+  static constexpr int PER_STAGE = PER_N + 1;
   // every wave's columns fall inside one 128-column scale block
   static constexpr bool ONE_NB =
       (128 % WN == 0) && ((BN % 128 == 0) || (128 % BN == 0));
   static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "tile shape");
   static_assert(BM % 8 == 0 && BN % 8 == 0, "direct-load blocks");
-  static_assert(BM + NBV <= S_FLOATS, "scale slots");
+  static_assert(BM + NBV <= S_FLOATS && S_WAVES <= W, "scale slots");
+  static_assert(PER_N >= 1, "every wave copies operand bytes");
   static_assert(STAGES >= 2 && (STAGES - 2) * PER_STAGE < 64, "pipeline depth");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
 };
@@ -248,15 +264,17 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
     dma16<C::B_NT ? 2 : 0>(c.Bg + (size_t)n * c.K + kb * kBlockK + ch * 16,
                            st + C::A_BYTES + cb * 1024);
   }
-  const int s = c.wave * 64 + c.lane;
-  const float* src;
-  if (s < C::BM)
-    src = c.sA + (size_t)(c.a_row0 + min(s, c.rows - 1)) * c.nkb + kb;
-  else if (s < C::BM + C::NBV)
-    src = c.sBg + (size_t)min(c.nb_first + s - C::BM, c.nnb - 1) * c.nkb + kb;
-  else
-    src = c.sA + (size_t)c.a_row0 * c.nkb + kb;
-  dma4(src, st + C::A_BYTES + C::B_BYTES + c.wave * 256);
+  if (c.wave < C::S_WAVES) {
+    const int s = c.wave * 64 + c.lane;
+    const float* src;
+    if (s < C::BM)
+      src = c.sA + (size_t)(c.a_row0 + min(s, c.rows - 1)) * c.nkb + kb;
+    else if (s < C::BM + C::NBV)
+      src = c.sBg + (size_t)min(c.nb_first + s - C::BM, c.nnb - 1) * c.nkb + kb;
+    else
+      src = c.sA + (size_t)c.a_row0 * c.nkb + kb;
+    dma4(src, st + C::A_BYTES + C::B_BYTES + c.wave * 256);
+  }
 }
 
 // MFMA block partials of one staged K block, promoted into acc.
@@ -361,7 +379,7 @@ template <int KIND, class C>
 __global__ void __launch_bounds__(C::NT)
 gemm_fp8_kernel(GemmArgs p) {
   constexpr int WM = C::WM, WN = C::WN, TI = C::TI, TJ = C::TJ;
-  constexpr int STAGES = C::STAGES, PER = C::PER_STAGE;
+  constexpr int STAGES = C::STAGES;
   // The kernel's only LDS variable: a second one would make the compiler tag LDS
   // accesses with per-variable alias scopes, dropping the restrict scopes that keep it
   // from waiting on in-flight stage copies (see kb_step).
@@ -429,7 +447,7 @@ gemm_fp8_kernel(GemmArgs p) {
       for (int it = 1 - STAGES; it < nk; ++it) {
         if (it >= 0) {
           // block `it` has landed once only the blocks issued after it are in flight
-          wait_stages_ahead<PER, STAGES - 2>(min(STAGES - 2, nk - 1 - it));
+          wait_stage_copies<C, STAGES - 2>(wave, min(STAGES - 2, nk - 1 - it));
           stage_barrier();
         }
         const int nxt = it + STAGES - 1;
@@ -495,7 +513,7 @@ __device__ __forceinline__ long stream_start(long g, long W, long G) { return g 
 template <class C>
 __global__ void __launch_bounds__(C::NT)
 gemm_fp8_stream_kernel(GemmArgs p) {
-  constexpr int TI = C::TI, TJ = C::TJ, STAGES = C::STAGES, PER = C::PER_STAGE;
+  constexpr int TI = C::TI, TJ = C::TJ, STAGES = C::STAGES;
   constexpr int FRAG_FLOATS = 64 * 4;                        // one 16x16 fp32 sub-tile
   constexpr int WAVE_SLOT = TI * TJ * FRAG_FLOATS;           // one wave's partial
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * C::STAGE_BYTES];
@@ -552,7 +570,7 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   int shared_tile[2] = {-1, -1};
   for (int step = 1 - STAGES; step < n_iter; ++step) {
     if (step >= 0) {
-      wait_stages_ahead<PER, STAGES - 2>(min(STAGES - 2, n_iter - 1 - step));
+      wait_stage_copies<C, STAGES - 2>(wave, min(STAGES - 2, n_iter - 1 - step));
       stage_barrier();
     }
     const bool issue = step + STAGES - 1 < n_iter;
