@@ -20,9 +20,11 @@ Recipe (identical for every consumer):
     standard normal float32; with ``outliers`` each entry is replaced, with
     probability 0.01, by 30 times a fresh standard normal (a heavy-tailed
     population that exercises per-block scaling).
-  * Quantisation: per block, amax = max |x| (fp32), scale = amax / 448 (fp32;
-    1 when amax == 0), code = e4m3fn(x / scale) with round-to-nearest-even,
-    saturating at +-448.  A uses 1x128 blocks along K (one scale per row and K block);
+  * Quantisation: per block, amax = max |x| (fp32), scale = amax / FMAX (fp32;
+    1 when amax == 0), code = fp8(x / scale) with round-to-nearest-even, saturating
+    at +-FMAX; the 8-bit format is E4M3 ("fn", FMAX = 448) by default, or E5M2
+    (FMAX = 57344), the other input format the aisharenet.com/ja usage guide names
+    (main functions, section 1).  A uses 1x128 blocks along K (one scale per row and K block);
     B uses 128x128 blocks (one scale per 128 rows of B, i.e. 128 output columns, and K
     block).  A final partial block (N not a multiple of 128) takes its amax over the
     rows that exist.
@@ -37,7 +39,10 @@ import numpy as np
 import torch
 
 E4M3_MAX = 448.0
+E5M2_MAX = 57344.0
 BLOCK = 128
+FP8_MAX = {"e4m3": E4M3_MAX, "e5m2": E5M2_MAX}
+FP8_DTYPE = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
 
 # tensor tags for the per-tensor random streams
 _TAG_A = 1
@@ -85,9 +90,15 @@ def normal_matrix(seed: int, tag: int, rows: int, cols: int, outliers: bool = Fa
     return out
 
 
+def fp8_encode(x: torch.Tensor, fmt: str = "e4m3") -> torch.Tensor:
+    """fp32 -> fp8 bytes (E4M3 or E5M2), round-to-nearest-even, saturating."""
+    m = FP8_MAX[fmt]
+    return x.clamp(-m, m).to(FP8_DTYPE[fmt]).view(torch.uint8)
+
+
 def e4m3fn_encode(x: torch.Tensor) -> torch.Tensor:
     """fp32 -> e4m3fn bytes, round-to-nearest-even, saturating at +-448."""
-    return x.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    return fp8_encode(x, "e4m3")
 
 
 def _pad_to(t: torch.Tensor, rows: int, cols: int) -> torch.Tensor:
@@ -98,31 +109,31 @@ def _pad_to(t: torch.Tensor, rows: int, cols: int) -> torch.Tensor:
     return out
 
 
-def _scale_of(amax: torch.Tensor) -> torch.Tensor:
-    return torch.where(amax == 0, torch.ones_like(amax), amax / E4M3_MAX)
+def _scale_of(amax: torch.Tensor, fmt: str = "e4m3") -> torch.Tensor:
+    return torch.where(amax == 0, torch.ones_like(amax), amax / FP8_MAX[fmt])
 
 
-def quantize_1x128(x: np.ndarray):
+def quantize_1x128(x: np.ndarray, fmt: str = "e4m3"):
     """Per-row, per-128-wide-K-block quantisation of a rows x K float32 matrix.
 
     Returns (codes uint8 rows x K, scales float32 rows x ceil(K/128))."""
     rows, K = x.shape
     nkb = -(-K // BLOCK)
     t = _pad_to(torch.from_numpy(x), rows, nkb * BLOCK).view(rows, nkb, BLOCK)
-    scales = _scale_of(t.abs().amax(dim=2))                        # rows x nkb
-    codes = e4m3fn_encode(t / scales[:, :, None]).view(rows, nkb * BLOCK)[:, :K]
+    scales = _scale_of(t.abs().amax(dim=2), fmt)                   # rows x nkb
+    codes = fp8_encode(t / scales[:, :, None], fmt).view(rows, nkb * BLOCK)[:, :K]
     return np.ascontiguousarray(codes.numpy()), scales.numpy()
 
 
-def quantize_128x128(x: np.ndarray):
+def quantize_128x128(x: np.ndarray, fmt: str = "e4m3"):
     """Per 128x128 block quantisation of an N x K float32 matrix (B stored N x K).
 
     Returns (codes uint8 N x K, scales float32 ceil(N/128) x ceil(K/128))."""
     N, K = x.shape
     nnb, nkb = -(-N // BLOCK), -(-K // BLOCK)
     t = _pad_to(torch.from_numpy(x), nnb * BLOCK, nkb * BLOCK).view(nnb, BLOCK, nkb, BLOCK)
-    scales = _scale_of(t.abs().amax(dim=(1, 3)))                   # nnb x nkb
-    codes = e4m3fn_encode(t / scales[:, None, :, None]).view(nnb * BLOCK, nkb * BLOCK)
+    scales = _scale_of(t.abs().amax(dim=(1, 3)), fmt)              # nnb x nkb
+    codes = fp8_encode(t / scales[:, None, :, None], fmt).view(nnb * BLOCK, nkb * BLOCK)
     return np.ascontiguousarray(codes[:N, :K].numpy()), scales.numpy()
 
 
@@ -149,41 +160,45 @@ class Problem:
     sizes: list | None = None
     seed: int = 0
     meta: dict = field(default_factory=dict)
+    a_fmt: str = "e4m3"     # operand formats: "e4m3" or "e5m2"
+    b_fmt: str = "e4m3"
 
     @property
     def rows(self) -> int:
         return self.A.shape[0]
 
 
-def _quant_B(seed: int, G: int, N: int, K: int, outliers: bool):
+def _quant_B(seed: int, G: int, N: int, K: int, outliers: bool, fmt: str = "e4m3"):
     Bs, sBs = [], []
     for g in range(G):
         b = normal_matrix(seed, _TAG_B + 16 * g, N, K, outliers)
-        q, s = quantize_128x128(b)
+        q, s = quantize_128x128(b, fmt)
         Bs.append(q)
         sBs.append(s)
     return np.concatenate(Bs, 0), np.concatenate(sBs, 0)
 
 
-def make_dense(M: int, N: int, K: int, seed: int, outliers: bool = False) -> Problem:
+def make_dense(M: int, N: int, K: int, seed: int, outliers: bool = False,
+               a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> Problem:
     a = normal_matrix(seed, _TAG_A, M, K, outliers)
-    A, sA = quantize_1x128(a)
+    A, sA = quantize_1x128(a, a_fmt)
     del a
-    B, sB = _quant_B(seed, 1, N, K, outliers)
-    return Problem("dense", M, N, K, 1, A, sA, B, sB, seed=seed)
+    B, sB = _quant_B(seed, 1, N, K, outliers, b_fmt)
+    return Problem("dense", M, N, K, 1, A, sA, B, sB, seed=seed, a_fmt=a_fmt, b_fmt=b_fmt)
 
 
-def make_contiguous(sizes, N: int, K: int, seed: int) -> Problem:
+def make_contiguous(sizes, N: int, K: int, seed: int, a_fmt: str = "e4m3",
+                    b_fmt: str = "e4m3") -> Problem:
     sizes = [int(s) for s in sizes]
     G = len(sizes)
     rows = sum(sizes)
     a = normal_matrix(seed, _TAG_A, rows, K)
-    A, sA = quantize_1x128(a)
+    A, sA = quantize_1x128(a, a_fmt)
     del a
-    B, sB = _quant_B(seed, G, N, K, False)
+    B, sB = _quant_B(seed, G, N, K, False, b_fmt)
     gi = group_sizes_to_idx(sizes)
     return Problem("contiguous", rows, N, K, G, A, sA, B, sB, group_idx=gi, sizes=sizes,
-                   seed=seed)
+                   seed=seed, a_fmt=a_fmt, b_fmt=b_fmt)
 
 
 def random_contiguous_sizes(seed: int, G: int = 8, align: int = 128, max_blocks: int = 64):
@@ -192,16 +207,18 @@ def random_contiguous_sizes(seed: int, G: int = 8, align: int = 128, max_blocks:
     return [int(v) * align for v in rng.integers(1, max_blocks + 1, size=G)]
 
 
-def make_masked(G: int, cap: int, N: int, K: int, seed: int, masked_m=None) -> Problem:
+def make_masked(G: int, cap: int, N: int, K: int, seed: int, masked_m=None,
+                a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> Problem:
     if masked_m is None:
         rng = np.random.default_rng(seed)
         masked_m = rng.integers(0, cap + 1, size=G)
     masked_m = np.asarray(masked_m, dtype=np.int32)
     a = normal_matrix(seed, _TAG_A, G * cap, K)
-    A, sA = quantize_1x128(a)
+    A, sA = quantize_1x128(a, a_fmt)
     del a
-    B, sB = _quant_B(seed, G, N, K, False)
-    return Problem("masked", cap, N, K, G, A, sA, B, sB, masked_m=masked_m, seed=seed)
+    B, sB = _quant_B(seed, G, N, K, False, b_fmt)
+    return Problem("masked", cap, N, K, G, A, sA, B, sB, masked_m=masked_m, seed=seed,
+                   a_fmt=a_fmt, b_fmt=b_fmt)
 
 
 # --------------------------------------------------------------------------------------
@@ -259,20 +276,30 @@ def masked_cases():
 
 def make(case: dict) -> Problem:
     k = case["kind"]
+    fmts = dict(a_fmt=case.get("a_fmt", "e4m3"), b_fmt=case.get("b_fmt", "e4m3"))
     if k == "dense":
-        return make_dense(case["M"], case["N"], case["K"], case["seed"], case.get("outliers", False))
+        return make_dense(case["M"], case["N"], case["K"], case["seed"],
+                          case.get("outliers", False), **fmts)
     if k == "contiguous":
-        return make_contiguous(case["sizes"], case["N"], case["K"], case["seed"])
+        return make_contiguous(case["sizes"], case["N"], case["K"], case["seed"], **fmts)
     if k == "masked":
         return make_masked(case["G"], case["cap"], case["N"], case["K"], case["seed"],
-                           case.get("masked_m"))
+                           case.get("masked_m"), **fmts)
     raise ValueError(k)
+
+
+def with_formats(cases, a_fmt: str, b_fmt: str):
+    """The same cases with other operand formats (the draws are unchanged)."""
+    return [dict(c, a_fmt=a_fmt, b_fmt=b_fmt) for c in cases]
 
 
 def case_name(case: dict) -> str:
     k = case["kind"]
+    fm = ""
+    if case.get("a_fmt", "e4m3") != "e4m3" or case.get("b_fmt", "e4m3") != "e4m3":
+        fm = f"_{case.get('a_fmt', 'e4m3')}x{case.get('b_fmt', 'e4m3')}"
     if k == "dense":
-        return f"dense_{case['M']}x{case['N']}x{case['K']}"
+        return f"dense_{case['M']}x{case['N']}x{case['K']}{fm}"
     if k == "contiguous":
-        return f"contig_{case.get('name', len(case['sizes']))}_{case['N']}x{case['K']}"
-    return f"masked_{case['G']}x{case['cap']}_{case['N']}x{case['K']}"
+        return f"contig_{case.get('name', len(case['sizes']))}_{case['N']}x{case['K']}{fm}"
+    return f"masked_{case['G']}x{case['cap']}_{case['N']}x{case['K']}{fm}"

@@ -42,11 +42,17 @@ def _load():
         lib.dgref_bf16_rne.restype = ctypes.c_uint16
         lib.dgref_bf16_rne.argtypes = [ctypes.c_double]
         lib.dgref_threads.restype = ctypes.c_int
-        lib.dgref_gemm_fp8_nt.argtypes = [P, P, P, P, P, P, I64, I64, I64]
-        lib.dgref_grouped_contiguous.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64]
-        lib.dgref_grouped_masked.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64]
+        I = ctypes.c_int
+        lib.dgref_gemm_fp8_nt_fmt.restype = I
+        lib.dgref_gemm_fp8_nt_fmt.argtypes = [P, I, P, P, I, P, P, P, I64, I64, I64]
+        lib.dgref_grouped_contiguous_fmt.restype = I
+        lib.dgref_grouped_contiguous_fmt.argtypes = [P, I, P, P, I, P, P, P, P, I64, I64, I64,
+                                                     I64]
+        lib.dgref_grouped_masked_fmt.restype = I
+        lib.dgref_grouped_masked_fmt.argtypes = [P, I, P, P, I, P, P, P, P, I64, I64, I64, I64]
         lib.dgref_bf16_rne_array.argtypes = [P, P, I64]
         lib.dgref_e4m3fn_decode_array.argtypes = [P, P, I64]
+        lib.dgref_e5m2_decode_array.argtypes = [P, P, I64]
         _lib = lib
     return _lib
 
@@ -71,6 +77,23 @@ def decode_e4m3fn(codes) -> np.ndarray:
     return out
 
 
+def decode_e5m2(codes) -> np.ndarray:
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    _load().dgref_e5m2_decode_array(_p(codes), _p(out), codes.size)
+    return out
+
+
+FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+def _fmt(f) -> int:
+    """Operand format: 'e4m3' (E4M3, the default) or 'e5m2'."""
+    if f not in FORMATS:
+        raise ValueError(f"unknown operand format {f!r}")
+    return FORMATS[f]
+
+
 def bf16_rne(x) -> np.ndarray:
     x = _c(x, np.float64)
     out = np.empty(x.shape, dtype=np.uint16)
@@ -87,9 +110,10 @@ def _prep_out(C, shape, want_acc):
     return C, acc
 
 
-def gemm_fp8_nt(A, sA, B, sB, C=None, want_acc=False):
+def gemm_fp8_nt(A, sA, B, sB, C=None, want_acc=False, a_fmt="e4m3", b_fmt="e4m3"):
     """Dense NT GEMM.  A: M x K uint8, sA: M x ceil(K/128) f32, B: N x K uint8,
-    sB: ceil(N/128) x ceil(K/128) f32.  Returns C (M x N bf16 bits)[, fp64 values]."""
+    sB: ceil(N/128) x ceil(K/128) f32; a_fmt / b_fmt: 'e4m3' or 'e5m2' codes.
+    Returns C (M x N bf16 bits)[, fp64 values]."""
     A, B = _c(A, np.uint8), _c(B, np.uint8)
     sA, sB = _c(sA, np.float32), _c(sB, np.float32)
     M, K = A.shape
@@ -97,11 +121,13 @@ def gemm_fp8_nt(A, sA, B, sB, C=None, want_acc=False):
     nkb = -(-K // 128)
     assert B.shape[1] == K and sA.shape == (M, nkb) and sB.shape == (-(-N // 128), nkb)
     C, acc = _prep_out(C, (M, N), want_acc)
-    _load().dgref_gemm_fp8_nt(_p(A), _p(sA), _p(B), _p(sB), _p(C), _p(acc), M, N, K)
+    _load().dgref_gemm_fp8_nt_fmt(_p(A), _fmt(a_fmt), _p(sA), _p(B), _fmt(b_fmt), _p(sB),
+                                  _p(C), _p(acc), M, N, K)
     return (C, acc) if want_acc else C
 
 
-def grouped_contiguous(A, sA, B, sB, group_idx, G, C=None, want_acc=False):
+def grouped_contiguous(A, sA, B, sB, group_idx, G, C=None, want_acc=False, a_fmt="e4m3",
+                       b_fmt="e4m3"):
     """Contiguous grouped NT GEMM.  A: M_total x K, B: G*N x K (G stacked N x K),
     sB: G*ceil(N/128) x ceil(K/128), group_idx: M_total int32."""
     A, B = _c(A, np.uint8), _c(B, np.uint8)
@@ -113,12 +139,13 @@ def grouped_contiguous(A, sA, B, sB, group_idx, G, C=None, want_acc=False):
     assert B.shape == (G * N, K) and sA.shape == (M, nkb) and gi.shape == (M,)
     assert sB.shape == (G * -(-N // 128), nkb)
     C, acc = _prep_out(C, (M, N), want_acc)
-    _load().dgref_grouped_contiguous(_p(A), _p(sA), _p(B), _p(sB), _p(gi), _p(C), _p(acc),
-                                     M, N, K, G)
+    _load().dgref_grouped_contiguous_fmt(_p(A), _fmt(a_fmt), _p(sA), _p(B), _fmt(b_fmt), _p(sB),
+                                         _p(gi), _p(C), _p(acc), M, N, K, G)
     return (C, acc) if want_acc else C
 
 
-def grouped_masked(A, sA, B, sB, masked_m, G, cap, C=None, want_acc=False):
+def grouped_masked(A, sA, B, sB, masked_m, G, cap, C=None, want_acc=False, a_fmt="e4m3",
+                   b_fmt="e4m3"):
     """Masked grouped NT GEMM.  A: G*cap x K, B: G*N x K, masked_m: G int32.
     C: G*cap x N; rows past masked_m[g] keep whatever C held."""
     A, B = _c(A, np.uint8), _c(B, np.uint8)
@@ -130,6 +157,6 @@ def grouped_masked(A, sA, B, sB, masked_m, G, cap, C=None, want_acc=False):
     assert A.shape == (G * cap, K) and B.shape == (G * N, K) and mm.shape == (G,)
     assert sA.shape == (G * cap, nkb) and sB.shape == (G * -(-N // 128), nkb)
     C, acc = _prep_out(C, (G * cap, N), want_acc)
-    _load().dgref_grouped_masked(_p(A), _p(sA), _p(B), _p(sB), _p(mm), _p(C), _p(acc),
-                                 G, cap, N, K)
+    _load().dgref_grouped_masked_fmt(_p(A), _fmt(a_fmt), _p(sA), _p(B), _fmt(b_fmt), _p(sB),
+                                     _p(mm), _p(C), _p(acc), G, cap, N, K)
     return (C, acc) if want_acc else C

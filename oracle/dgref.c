@@ -23,11 +23,19 @@
  *     section on grouped GEMM for MoE; contiguous and masked layouts: flashmla.org/zh
  *     page, section "DeepGEMM performance", and the usage guide's sections 2 and 3.
  *
- * Precision: the block partial is summed in fp64 and is exact (each e4m3 product has
- * at most 8 significant bits and magnitude in [2^-18, 448^2]; 128 of them stay below
- * 2^25, i.e. within 43 bits).  sA*sB is exact in fp64 (24+24 bits).  The scaled term
- * is rounded once to fp64, the K-block sum runs in fp64 in kb order 0,1,2,..., and the
- * result is rounded once, directly from fp64, to bf16 with round-to-nearest-even.
+ * Operand formats: E4M3 ("fn") by default; either operand may instead be E5M2, the
+ * other 8-bit format the aisharenet.com/ja usage guide names for the inputs (main
+ * functions, section 1).
+ *
+ * Precision: the block partial is exact.  With two E4M3 operands it is summed in fp64,
+ * which is exact (each product has at most 8 significant bits and magnitude in
+ * [2^-18, 448^2]; 128 of them stay below 2^25, i.e. within 43 bits).  An E5M2 operand
+ * widens the range (down to 2^-16, up to 57344), so such blocks are summed exactly in
+ * 128-bit integers (every E4M3 value is an integer times 2^-9, every E5M2 value an
+ * integer times 2^-16) and rounded once to fp64.  sA*sB is exact in fp64 (24+24 bits).
+ * The scaled term is rounded once to fp64, the K-block sum runs in fp64 in kb order
+ * 0,1,2,..., and the result is rounded once, directly from fp64, to bf16 with
+ * round-to-nearest-even.
  *
  * Readings where the pages are silent (each one is listed with its reason in the
  * design notes of this repository):
@@ -70,6 +78,24 @@ double dgref_e4m3fn_decode(uint8_t code)
     return sign ? -v : v;
 }
 
+/* OCP 8-bit floating point, E5M2.  Sign bit, 5-bit exponent with bias 15, 2-bit
+ * mantissa.  Exponent field 0 is subnormal: m * 2^-16.  Exponent field 31 holds the
+ * infinities (mantissa 0) and NaNs (mantissa != 0); the largest finite is 0x7B = 57344. */
+double dgref_e5m2_decode(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 2) & 0x1F;
+    int m = code & 3;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -16);                /* 0.m * 2^(1-15) */
+    else
+        v = ldexp((double)(4 + m), e - 17);       /* 1.m * 2^(e-15) */
+    return sign ? -v : v;
+}
+
 /* Round a double to the nearest bf16 (8 significant bits, 8 exponent bits, bias 127),
  * ties to even, in one step from the double value.  NaN -> 0x7FC0.  Overflow past the
  * largest finite bf16 rounds to infinity, as round-to-nearest requires. */
@@ -100,22 +126,65 @@ uint16_t dgref_bf16_rne(double x)
     return (uint16_t)(cv.u >> 16);
 }
 
-static double g_dec[256];
+#define DGREF_E4M3 0
+#define DGREF_E5M2 1
+
+/* Decoded values per format, and for the integer path each finite value as an integer
+ * times 2^-LSB_EXP (E4M3: 2^-9, E5M2: 2^-16); the integer table is only read for finite
+ * codes (non-finite codes send the element down the fp64 path). */
+static double g_dec[2][256];
+static int64_t g_int[2][256];
+static int g_fin[2][256];
+static const int g_lsb_exp[2] = {9, 16};
 static int g_dec_ready = 0;
 
 static void build_decode_table(void)
 {
-    int c;
+    int c, f;
     if (g_dec_ready)
         return;
-    for (c = 0; c < 256; ++c)
-        g_dec[c] = dgref_e4m3fn_decode((uint8_t)c);
+    for (c = 0; c < 256; ++c) {
+        g_dec[DGREF_E4M3][c] = dgref_e4m3fn_decode((uint8_t)c);
+        g_dec[DGREF_E5M2][c] = dgref_e5m2_decode((uint8_t)c);
+    }
+    for (f = 0; f < 2; ++f)
+        for (c = 0; c < 256; ++c) {
+            double v = g_dec[f][c];
+            g_fin[f][c] = isfinite(v);
+            g_int[f][c] = g_fin[f][c] ? (int64_t)ldexp(v, g_lsb_exp[f]) : 0;  /* exact */
+        }
     g_dec_ready = 1;
 }
 
+/* The exact partial of one K block when an operand is E5M2: the integer sum of the
+ * integer products, then one rounding to fp64.  Falls back to the fp64 sum (which then
+ * carries the infinities/NaNs) when a code is not finite. */
+static double block_partial_wide(const uint8_t *a, int fa, const uint8_t *b, int fb,
+                                 int64_t k0, int64_t k1)
+{
+    __int128 s = 0;
+    int64_t k;
+    double partial = 0.0;
+    for (k = k0; k < k1; ++k)
+        if (!g_fin[fa][a[k]] || !g_fin[fb][b[k]]) {
+            for (k = k0; k < k1; ++k)
+                partial += g_dec[fa][a[k]] * g_dec[fb][b[k]];
+            return partial;
+        }
+    for (k = k0; k < k1; ++k)
+        s += (__int128)g_int[fa][a[k]] * (__int128)g_int[fb][b[k]];   /* < 2^64 each */
+    /* |s| < 2^71: split into two exactly representable halves, rounded once on adding */
+    {
+        int64_t hi = (int64_t)(s >> 32);
+        uint64_t lo = (uint64_t)(s & 0xFFFFFFFFu);
+        double v = ldexp((double)hi, 32) + (double)lo;   /* one rounding */
+        return ldexp(v, -(g_lsb_exp[fa] + g_lsb_exp[fb]));
+    }
+}
+
 /* The unrounded fp64 result of one output element: the two-level sum above. */
-static double element_f64(const uint8_t *a_row, const float *sa_row,
-                          const uint8_t *b_row, const float *sb_row, int64_t K)
+static double element_f64(const uint8_t *a_row, int fa, const float *sa_row,
+                          const uint8_t *b_row, int fb, const float *sb_row, int64_t K)
 {
     int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
     double acc = 0.0;
@@ -125,8 +194,12 @@ static double element_f64(const uint8_t *a_row, const float *sa_row,
         int64_t k1 = k0 + DGREF_BLOCK < K ? k0 + DGREF_BLOCK : K;
         double partial = 0.0;
         double s;
-        for (k = k0; k < k1; ++k)
-            partial += g_dec[a_row[k]] * g_dec[b_row[k]];
+        if (fa == DGREF_E4M3 && fb == DGREF_E4M3) {
+            for (k = k0; k < k1; ++k)
+                partial += g_dec[fa][a_row[k]] * g_dec[fb][b_row[k]];
+        } else {
+            partial = block_partial_wide(a_row, fa, b_row, fb, k0, k1);
+        }
         s = (double)sa_row[kb] * (double)sb_row[kb];
         acc += partial * s;
     }
@@ -135,20 +208,26 @@ static double element_f64(const uint8_t *a_row, const float *sa_row,
 
 /* One output row against one group's B.  acc_out (optional) receives the unrounded
  * fp64 values, c_out (optional) the bf16 bits. */
-static void one_row(const uint8_t *a_row, const float *sa_row, const uint8_t *B,
-                    const float *sB, int64_t N, int64_t K, uint16_t *c_out, double *acc_out)
+static void one_row(const uint8_t *a_row, int fa, const float *sa_row, const uint8_t *B,
+                    int fb, const float *sB, int64_t N, int64_t K, uint16_t *c_out,
+                    double *acc_out)
 {
     int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
     int64_t n;
     for (n = 0; n < N; ++n) {
         const uint8_t *b_row = B + n * K;
         const float *sb_row = sB + (n / DGREF_BLOCK) * nkb;
-        double v = element_f64(a_row, sa_row, b_row, sb_row, K);
+        double v = element_f64(a_row, fa, sa_row, b_row, fb, sb_row, K);
         if (acc_out)
             acc_out[n] = v;
         if (c_out)
             c_out[n] = dgref_bf16_rne(v);
     }
+}
+
+static int valid_formats(int fa, int fb)
+{
+    return (fa == DGREF_E4M3 || fa == DGREF_E5M2) && (fb == DGREF_E4M3 || fb == DGREF_E5M2);
 }
 
 int dgref_threads(void)
@@ -160,31 +239,44 @@ int dgref_threads(void)
 #endif
 }
 
-/* Dense: C (M x N bf16) = A (M x K) x B (N x K)^T with the block scales.
- * acc (optional, M x N doubles) receives the unrounded values. */
+/* Dense: C (M x N bf16) = A (M x K) x B (N x K)^T with the block scales; fa / fb are
+ * the operand formats (0: E4M3, 1: E5M2).  acc (optional, M x N doubles) receives the
+ * unrounded values.  Returns -1 for an unknown format, else 0. */
+int dgref_gemm_fp8_nt_fmt(const uint8_t *A, int fa, const float *sA, const uint8_t *B,
+                          int fb, const float *sB, uint16_t *C, double *acc,
+                          int64_t M, int64_t N, int64_t K)
+{
+    int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
+    int64_t m;
+    if (!valid_formats(fa, fb))
+        return -1;
+    build_decode_table();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; ++m)
+        one_row(A + m * K, fa, sA + m * nkb, B, fb, sB, N, K,
+                C ? C + m * N : 0, acc ? acc + m * N : 0);
+    return 0;
+}
+
 void dgref_gemm_fp8_nt(const uint8_t *A, const float *sA, const uint8_t *B,
                        const float *sB, uint16_t *C, double *acc,
                        int64_t M, int64_t N, int64_t K)
 {
-    int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
-    int64_t m;
-    build_decode_table();
-#pragma omp parallel for schedule(dynamic, 1)
-    for (m = 0; m < M; ++m)
-        one_row(A + m * K, sA + m * nkb, B, sB, N, K,
-                C ? C + m * N : 0, acc ? acc + m * N : 0);
+    dgref_gemm_fp8_nt_fmt(A, DGREF_E4M3, sA, B, DGREF_E4M3, sB, C, acc, M, N, K);
 }
 
 /* Contiguous grouped: rows of all groups concatenated (M_total x K); B is G x N x K,
  * sB is G x ceil(N/128) x ceil(K/128); group_idx is one int32 per row. */
-void dgref_grouped_contiguous(const uint8_t *A, const float *sA, const uint8_t *B,
-                              const float *sB, const int32_t *group_idx, uint16_t *C,
-                              double *acc, int64_t M_total, int64_t N, int64_t K,
-                              int64_t G)
+int dgref_grouped_contiguous_fmt(const uint8_t *A, int fa, const float *sA,
+                                 const uint8_t *B, int fb, const float *sB,
+                                 const int32_t *group_idx, uint16_t *C, double *acc,
+                                 int64_t M_total, int64_t N, int64_t K, int64_t G)
 {
     int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
     int64_t nnb = (N + DGREF_BLOCK - 1) / DGREF_BLOCK;
     int64_t m;
+    if (!valid_formats(fa, fb))
+        return -1;
     build_decode_table();
 #pragma omp parallel for schedule(dynamic, 1)
     for (m = 0; m < M_total; ++m) {
@@ -192,20 +284,32 @@ void dgref_grouped_contiguous(const uint8_t *A, const float *sA, const uint8_t *
         int32_t lead = group_idx[(m / DGREF_BLOCK) * DGREF_BLOCK];
         if (g < 0 || g >= G || g != lead)
             continue;                             /* row left untouched */
-        one_row(A + m * K, sA + m * nkb, B + (int64_t)g * N * K, sB + (int64_t)g * nnb * nkb,
-                N, K, C ? C + m * N : 0, acc ? acc + m * N : 0);
+        one_row(A + m * K, fa, sA + m * nkb, B + (int64_t)g * N * K, fb,
+                sB + (int64_t)g * nnb * nkb, N, K, C ? C + m * N : 0, acc ? acc + m * N : 0);
     }
+    return 0;
+}
+
+void dgref_grouped_contiguous(const uint8_t *A, const float *sA, const uint8_t *B,
+                              const float *sB, const int32_t *group_idx, uint16_t *C,
+                              double *acc, int64_t M_total, int64_t N, int64_t K,
+                              int64_t G)
+{
+    dgref_grouped_contiguous_fmt(A, DGREF_E4M3, sA, B, DGREF_E4M3, sB, group_idx, C, acc,
+                                 M_total, N, K, G);
 }
 
 /* Masked grouped: A is G x cap x K, C is G x cap x N; group g computes its first
  * clamp(masked_m[g], 0, cap) rows and leaves the rest of C untouched. */
-void dgref_grouped_masked(const uint8_t *A, const float *sA, const uint8_t *B,
-                          const float *sB, const int32_t *masked_m, uint16_t *C,
-                          double *acc, int64_t G, int64_t cap, int64_t N, int64_t K)
+int dgref_grouped_masked_fmt(const uint8_t *A, int fa, const float *sA, const uint8_t *B,
+                             int fb, const float *sB, const int32_t *masked_m, uint16_t *C,
+                             double *acc, int64_t G, int64_t cap, int64_t N, int64_t K)
 {
     int64_t nkb = (K + DGREF_BLOCK - 1) / DGREF_BLOCK;
     int64_t nnb = (N + DGREF_BLOCK - 1) / DGREF_BLOCK;
     int64_t i;
+    if (!valid_formats(fa, fb))
+        return -1;
     build_decode_table();
 #pragma omp parallel for schedule(dynamic, 1)
     for (i = 0; i < G * cap; ++i) {
@@ -217,9 +321,18 @@ void dgref_grouped_masked(const uint8_t *A, const float *sA, const uint8_t *B,
             valid = cap;
         if (m >= valid)
             continue;                             /* row left untouched */
-        one_row(A + i * K, sA + i * nkb, B + g * N * K, sB + g * nnb * nkb, N, K,
+        one_row(A + i * K, fa, sA + i * nkb, B + g * N * K, fb, sB + g * nnb * nkb, N, K,
                 C ? C + i * N : 0, acc ? acc + i * N : 0);
     }
+    return 0;
+}
+
+void dgref_grouped_masked(const uint8_t *A, const float *sA, const uint8_t *B,
+                          const float *sB, const int32_t *masked_m, uint16_t *C,
+                          double *acc, int64_t G, int64_t cap, int64_t N, int64_t K)
+{
+    dgref_grouped_masked_fmt(A, DGREF_E4M3, sA, B, DGREF_E4M3, sB, masked_m, C, acc, G, cap,
+                             N, K);
 }
 
 /* Element-wise helpers for the tests. */
@@ -235,4 +348,11 @@ void dgref_e4m3fn_decode_array(const uint8_t *codes, double *out, int64_t n)
     int64_t i;
     for (i = 0; i < n; ++i)
         out[i] = dgref_e4m3fn_decode(codes[i]);
+}
+
+void dgref_e5m2_decode_array(const uint8_t *codes, double *out, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i)
+        out[i] = dgref_e5m2_decode(codes[i]);
 }

@@ -57,14 +57,22 @@ def f32_to_bf16_bits_torch(x) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def e4m3_codes_of(values) -> np.ndarray:
-    """e4m3fn codes of values that are exactly representable (used to build integer
-    test inputs); raises if a value is not exact."""
+FP8_TORCH = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
+def fp8_codes_of(values, fmt: str = "e4m3") -> np.ndarray:
+    """fp8 codes (E4M3 or E5M2) of values that are exactly representable (used to build
+    integer test inputs); raises if a value is not exact."""
     v = torch.as_tensor(np.asarray(values, dtype=np.float32))
-    codes = v.to(torch.float8_e4m3fn)
+    codes = v.to(FP8_TORCH[fmt])
     back = codes.to(torch.float32)
-    assert torch.equal(back, v), "value not exact in e4m3fn"
+    assert torch.equal(back, v), f"value not exact in {fmt}"
     return codes.view(torch.uint8).numpy()
+
+
+def e4m3_codes_of(values) -> np.ndarray:
+    """e4m3fn codes of values that are exactly representable."""
+    return fp8_codes_of(values, "e4m3")
 
 
 def assert_within_tolerance(c_test_bits, c_ref_bits, written, what=""):

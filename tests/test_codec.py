@@ -1,8 +1,9 @@
-"""Pins for the oracle's two codecs: e4m3fn decoding and fp64 -> bf16 rounding.
+"""Pins for the oracle's codecs: e4m3fn and e5m2 decoding, fp64 -> bf16 rounding.
 
-The e4m3fn decode is checked against values fixed by the OCP 8-bit format definition
-and against torch's own float8_e4m3fn conversion; the bf16 rounding against torch's
-fp32 -> bfloat16 rounding (an independent implementation) and hand-made ties."""
+The fp8 decodes are checked against values fixed by the OCP 8-bit format definitions
+and against torch's own float8_e4m3fn / float8_e5m2 conversions; the bf16 rounding
+against torch's fp32 -> bfloat16 rounding (an independent implementation) and
+hand-made ties."""
 import math
 
 import numpy as np
@@ -35,6 +36,32 @@ def test_e4m3fn_decode_all_codes_match_torch():
     assert np.array_equal(np.isnan(ours), np.isnan(ref))
     assert np.array_equal(ours[~both_nan], ref[~both_nan])
     assert int(np.isnan(ours).sum()) == 2   # only S.1111.111
+
+
+def test_e5m2_decode_matches_format_definition():
+    expect = {
+        0x00: 0.0, 0x01: 2.0 ** -16, 0x03: 3 * 2.0 ** -16, 0x04: 2.0 ** -14,
+        0x3C: 1.0, 0x3D: 1.25, 0x3E: 1.5, 0x3F: 1.75, 0x40: 2.0, 0x7B: 57344.0,
+        0x7A: 49152.0, 0xBC: -1.0, 0xFB: -57344.0, 0x81: -(2.0 ** -16),
+    }
+    got = oracle.decode_e5m2(np.array(list(expect), dtype=np.uint8))
+    assert np.array_equal(got, np.array(list(expect.values())))
+    z = oracle.decode_e5m2(np.array([0x80], np.uint8))[0]
+    assert z == 0.0 and math.copysign(1.0, z) == -1.0
+    inf = oracle.decode_e5m2(np.array([0x7C, 0xFC], np.uint8))
+    assert inf[0] == math.inf and inf[1] == -math.inf
+    nan = oracle.decode_e5m2(np.array([0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF], np.uint8))
+    assert np.all(np.isnan(nan))
+
+
+def test_e5m2_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.decode_e5m2(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    both_nan = np.isnan(ours) & np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[~both_nan], ref[~both_nan])
+    assert int(np.isnan(ours).sum()) == 6 and int(np.isinf(ours).sum()) == 2
 
 
 def test_bf16_rne_matches_torch_on_fp32_values():

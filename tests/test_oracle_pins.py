@@ -13,6 +13,9 @@ Each test checks the oracle against something other than itself:
       contiguous with G=1 = dense, contiguous = per-segment dense calls)
   P8  NumPy fp64 matmul of torch-decoded values with unit scales, and a blockwise
       einsum with scales
+P2 and P3 also run with E5M2 operands (either or both), the other input format the
+aisharenet.com/ja usage guide names (main functions, section 1); one pin plants a block
+whose exact partial needs more than fp64's 53 bits.
 A plausible mistake in the oracle (dropped K block, wrong scale index, transposed
 operand, wrong sign, double rounding, wrong group) fails at least one of these."""
 from fractions import Fraction
@@ -23,20 +26,26 @@ import torch
 
 import oracle
 from moe_grouped_gemm_lhs_amd import inputs as I
-from tests.helpers import (SENTINEL, bf16_to_f64, e4m3_codes_of, read_sections,
-                           rows_written_contiguous, rows_written_masked)
+from tests.helpers import (FP8_TORCH, SENTINEL, bf16_to_f64, e4m3_codes_of, fp8_codes_of,
+                           read_sections, rows_written_contiguous, rows_written_masked)
+
+FMT_PAIRS = [("e4m3", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")]
+LSB_EXP = {"e4m3": 9, "e5m2": 16}   # every finite value is an integer times 2^-LSB_EXP
 
 
-def torch_decode(codes) -> np.ndarray:
-    """Independent e4m3fn decoding through torch (not the oracle's table)."""
+def torch_decode(codes, fmt: str = "e4m3") -> np.ndarray:
+    """Independent fp8 decoding through torch (not the oracle's table)."""
     return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(
-        torch.float8_e4m3fn).to(torch.float64).numpy()
+        FP8_TORCH[fmt]).to(torch.float64).numpy()
 
 
-def random_codes(rng, shape):
-    """Random e4m3fn bytes, excluding the two NaN codes."""
+def random_codes(rng, shape, fmt: str = "e4m3"):
+    """Random fp8 bytes, excluding the NaN (and, for E5M2, infinity) codes."""
     c = rng.integers(0, 256, size=shape, dtype=np.uint8)
-    c[(c & 0x7F) == 0x7F] = 0x7E
+    if fmt == "e4m3":
+        c[(c & 0x7F) == 0x7F] = 0x7E
+    else:
+        c[(c & 0x7C) == 0x7C] = (c[(c & 0x7C) == 0x7C] & 0x80) | 0x7B
     return c
 
 
@@ -66,13 +75,14 @@ def _bf16_fraction(bits: int) -> Fraction:
     return Fraction(float(bf16_to_f64(np.array([bits], np.uint16))[0]))
 
 
-def _exact_results(A, sA, B, sB):
+def _exact_results(A, sA, B, sB, a_fmt="e4m3", b_fmt="e4m3"):
     """Exact rational C (list of lists) and the sum of |terms| per element."""
     M, K = A.shape
     N = B.shape[0]
     nkb = -(-K // 128)
-    ia = np.rint(torch_decode(A) * 512).astype(np.int64)      # multiples of 2^-9
-    ib = np.rint(torch_decode(B) * 512).astype(np.int64)
+    la, lb = LSB_EXP[a_fmt], LSB_EXP[b_fmt]
+    ia = [[int(round(v * 2 ** la)) for v in row] for row in torch_decode(A, a_fmt)]
+    ib = [[int(round(v * 2 ** lb)) for v in row] for row in torch_decode(B, b_fmt)]
     out, mag = [], []
     for m in range(M):
         row, mrow = [], []
@@ -80,7 +90,8 @@ def _exact_results(A, sA, B, sB):
             tot, tmag = Fraction(0), Fraction(0)
             for kb in range(nkb):
                 k0, k1 = kb * 128, min(K, kb * 128 + 128)
-                p = Fraction(int(np.dot(ia[m, k0:k1], ib[n, k0:k1])), 1 << 18)
+                p = Fraction(sum(x * y for x, y in zip(ia[m][k0:k1], ib[n][k0:k1])),
+                             1 << (la + lb))
                 s = Fraction(float(sA[m, kb])) * Fraction(float(sB[n // 128, kb]))
                 tot += p * s
                 tmag += abs(p * s)
@@ -114,15 +125,16 @@ def _check_nearest(bits: int, exact: Fraction, err: Fraction) -> bool:
 
 @pytest.mark.parametrize("M,N,K,seed", [(5, 7, 384, 1), (2, 260, 200, 2), (8, 8, 128, 3),
                                         (3, 130, 256, 4)])
-def test_p2_exact_rational_brute_force(M, N, K, seed):
+@pytest.mark.parametrize("a_fmt,b_fmt", FMT_PAIRS)
+def test_p2_exact_rational_brute_force(M, N, K, seed, a_fmt, b_fmt):
     rng = np.random.default_rng(seed)
     nkb = -(-K // 128)
-    A = random_codes(rng, (M, K))
-    B = random_codes(rng, (N, K))
+    A = random_codes(rng, (M, K), a_fmt)
+    B = random_codes(rng, (N, K), b_fmt)
     sA = random_scales(rng, (M, nkb))
     sB = random_scales(rng, (-(-N // 128), nkb))
-    C, acc = oracle.gemm_fp8_nt(A, sA, B, sB, want_acc=True)
-    exact, mag = _exact_results(A, sA, B, sB)
+    C, acc = oracle.gemm_fp8_nt(A, sA, B, sB, want_acc=True, a_fmt=a_fmt, b_fmt=b_fmt)
+    exact, mag = _exact_results(A, sA, B, sB, a_fmt, b_fmt)
     ambiguous = 0
     for m in range(M):
         for n in range(N):
@@ -134,6 +146,29 @@ def test_p2_exact_rational_brute_force(M, N, K, seed):
     assert ambiguous == 0, f"{ambiguous} elements lie within fp64 error of a bf16 midpoint"
 
 
+def test_p2_wide_partial_is_exact():
+    """E5M2 x E5M2: a block holding 57344^2, then 2^-32, then -57344^2 sums exactly to
+    2^-32 (a left-to-right fp64 sum would return 0); the same with the tiny product in
+    each of 128 positions of one block and 2^-32 scaled into the bf16 range."""
+    K = 128
+    big, tiny = 0x7B, 0x01                      # 57344 and 2^-16 in E5M2
+    for pos in (1, 5, 127):
+        a = np.zeros((1, K), np.uint8)
+        b = np.zeros((1, K), np.uint8)
+        a[0, 0], b[0, 0] = big, big
+        a[0, pos], b[0, pos] = tiny, tiny
+        neg = 2 if pos != 2 else 3
+        a[0, neg], b[0, neg] = big | 0x80, big  # -57344 * 57344
+        C, acc = oracle.gemm_fp8_nt(a, np.ones((1, 1), np.float32), b,
+                                    np.ones((1, 1), np.float32), want_acc=True,
+                                    a_fmt="e5m2", b_fmt="e5m2")
+        assert acc[0, 0] == 2.0 ** -32
+        C2 = oracle.gemm_fp8_nt(a, np.full((1, 1), 2.0 ** 30, np.float32), b,
+                                np.full((1, 1), 2.0 ** 2, np.float32), a_fmt="e5m2",
+                                b_fmt="e5m2")
+        assert bf16_to_f64(C2)[0, 0] == 1.0
+
+
 # ---------------------------------------------------------------------------- P3
 def _sparse_int_rows(rng, rows, K, nnz, lo=-4, hi=4):
     v = np.zeros((rows, K))
@@ -143,15 +178,17 @@ def _sparse_int_rows(rng, rows, K, nnz, lo=-4, hi=4):
     return v
 
 
-def test_p3_integer_inputs_exact():
+@pytest.mark.parametrize("a_fmt,b_fmt", FMT_PAIRS)
+def test_p3_integer_inputs_exact(a_fmt, b_fmt):
     rng = np.random.default_rng(7)
     M, N, K = 37, 300, 384
     a = _sparse_int_rows(rng, M, K, 8)
     b = rng.integers(-4, 5, size=(N, K)).astype(np.float64)
     ref = a.astype(np.int64) @ b.astype(np.int64).T
     assert np.abs(ref).max() <= 256
-    C = oracle.gemm_fp8_nt(e4m3_codes_of(a), np.ones((M, 3), np.float32), e4m3_codes_of(b),
-                           np.ones((3, 3), np.float32))
+    C = oracle.gemm_fp8_nt(fp8_codes_of(a, a_fmt), np.ones((M, 3), np.float32),
+                           fp8_codes_of(b, b_fmt), np.ones((3, 3), np.float32),
+                           a_fmt=a_fmt, b_fmt=b_fmt)
     assert np.array_equal(bf16_to_f64(C), ref.astype(np.float64))
 
 
