@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "contiguous", "masked", "small"])
     ap.add_argument("--shapes", default="", help="comma-separated subset of shape indices")
+    ap.add_argument("--formats", default="e4m3xe4m3",
+                    choices=["e4m3xe4m3", "e5m2xe5m2", "e4m3xe5m2", "e5m2xe4m3"],
+                    help="operand formats A x B (the workloads are quantised to them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches, not a graph")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
@@ -89,6 +92,9 @@ def main():
     dg.load_library()
 
     cases = workload_cases(args.workload)
+    a_fmt, b_fmt = args.formats.split("x")
+    if (a_fmt, b_fmt) != ("e4m3", "e4m3"):
+        cases = I.with_formats(cases, a_fmt, b_fmt)
     if args.shapes:
         keep = [int(s) for s in args.shapes.split(",")]
         cases = [cases[i] for i in keep]
@@ -106,6 +112,7 @@ def main():
     ws = torch.zeros(max(ws_need, 16), dtype=torch.uint8, device=dev)
     for case in cases:
         p = I.make(case)
+        fm = dict(a_format=p.a_fmt, b_format=p.b_fmt)
         nkb, nnb = p.K // 128, -(-p.N // 128)
         A = torch.from_numpy(p.A).to(dev)
         sA = torch.from_numpy(p.sA).to(dev)
@@ -114,20 +121,21 @@ def main():
         if p.kind == "dense":
             B, sB = B.view(p.N, p.K), sB.view(nnb, nkb)
             C = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
-            fn = (lambda A=A, sA=sA, B=B, sB=sB, C=C: dg.dg_gemm_fp8_nt(A, sA, B, sB, C, workspace=ws))
+            fn = (lambda A=A, sA=sA, B=B, sB=sB, C=C:
+                  dg.dg_gemm_fp8_nt(A, sA, B, sB, C, workspace=ws, **fm))
         elif p.kind == "contiguous":
             B, sB = B.view(p.G, p.N, p.K), sB.view(p.G, nnb, nkb)
             gi = torch.from_numpy(p.group_idx).to(dev)
             C = torch.empty((p.rows, p.N), dtype=torch.bfloat16, device=dev)
             fn = (lambda A=A, sA=sA, B=B, sB=sB, gi=gi, C=C:
-                  dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, gi, C, workspace=ws))
+                  dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, gi, C, workspace=ws, **fm))
         else:
             A, sA = A.view(p.G, p.M, p.K), sA.view(p.G, p.M, nkb)
             B, sB = B.view(p.G, p.N, p.K), sB.view(p.G, nnb, nkb)
             mm = torch.from_numpy(p.masked_m).to(dev)
             C = torch.empty((p.G, p.M, p.N), dtype=torch.bfloat16, device=dev)
             fn = (lambda A=A, sA=sA, B=B, sB=sB, mm=mm, C=C:
-                  dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, mm, C, workspace=ws))
+                  dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, mm, C, workspace=ws, **fm))
         flops, nbytes = work_of(p)
         kind_id = {"dense": 0, "contiguous": 1, "masked": 2}[p.kind]
         inst = dg.dg_instance_name(kind_id, p.M if p.kind != "contiguous" else p.rows, p.N, p.K, p.G)
@@ -236,9 +244,12 @@ def main():
         "metric": "FP8 TFLOPS and HBM GB/s (as % of MI355X peak) per M,N,K / group shape",
         "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3" if args.formats == "e4m3xe4m3" else "fp8" + args.formats,
         "data": "synthetic (seeded N(0,1), 1x128 / 128x128 e4m3fn block quantisation)",
-        "config": {"workload": WORKLOAD_TEXT[args.workload], "shapes": len(calls),
+        "config": {"workload": WORKLOAD_TEXT[args.workload]
+                   + ("" if args.formats == "e4m3xe4m3" else f", operands {args.formats}"),
+                   "shapes": len(calls),
                    "parallelism": "single GPU",
                    "step": "one HIP graph of all shapes" if graph is not None else "eager launches"},
         "tflops": round(total_flops / step_s / 1e12, 2),
@@ -317,11 +328,13 @@ def cpu_baseline(problems, calls, budget_s, hbm_bound, min_s=10.0):
 def _oracle_rows(p, r):
     import oracle
     nnb = -(-p.N // 128)
+    fm = dict(a_fmt=p.a_fmt, b_fmt=p.b_fmt)
     if p.kind == "dense":
-        return oracle.gemm_fp8_nt(p.A[:r], p.sA[:r], p.B, p.sB)
+        return oracle.gemm_fp8_nt(p.A[:r], p.sA[:r], p.B, p.sB, **fm)
     if p.kind == "contiguous":
-        return oracle.grouped_contiguous(p.A[:r], p.sA[:r], p.B, p.sB, p.group_idx[:r], p.G)
-    return oracle.gemm_fp8_nt(p.A[:r], p.sA[:r], p.B[:p.N], p.sB[:nnb])
+        return oracle.grouped_contiguous(p.A[:r], p.sA[:r], p.B, p.sB, p.group_idx[:r], p.G,
+                                         **fm)
+    return oracle.gemm_fp8_nt(p.A[:r], p.sA[:r], p.B[:p.N], p.sB[:nnb], **fm)
 
 
 if __name__ == "__main__":

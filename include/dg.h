@@ -1,5 +1,5 @@
 /*
- * dg.h -- C ABI of libdg, an FP8 (e4m3fn) block-scaled NT GEMM for AMD Instinct
+ * dg.h -- C ABI of libdg, an FP8 (E4M3 / E5M2) block-scaled NT GEMM for AMD Instinct
  * MI355X (gfx950) with BF16 output, in a dense form and two MoE grouped forms.
  *
  * What every call computes (for each written output element):
@@ -30,10 +30,12 @@
  *       A  e4m3fn bytes,   rows x K         sA fp32, rows x (K/128)
  *       B  e4m3fn bytes,   G x N x K        sB fp32, G x ceil(N/128) x (K/128)
  *       C  bf16 bits,      rows x N
- *     e4m3fn is the OCP 8-bit format E4M3 (bias 7, max 448, no infinities, NaN = S.1111.111).
+ *     e4m3fn is the OCP 8-bit format E4M3 (bias 7, max 448, no infinities, NaN = S.1111.111);
+ *     the _ex calls also take E5M2 for either operand.
  *     Column n of C uses row n/128 of its group's sB; N need not be a multiple of 128.
  *   - Preconditions checked on the host, before any device work, in this order:
  *       shapes: K > 0 and K % 128 == 0, M/N >= 0, G >= 1, cap >= 0  -> DG_ERR_SHAPE
+ *       operand formats (the _ex calls) DG_FP8_E4M3 or DG_FP8_E5M2  -> DG_ERR_FORMAT
  *       an empty output (no rows or N == 0) returns DG_OK without touching anything
  *       pointers non-NULL                                         -> DG_ERR_NULL
  *       A, B, C 16-byte aligned; sA, sB, group_idx, masked_m 4-byte -> DG_ERR_ALIGN
@@ -70,6 +72,13 @@ typedef int dg_status;
 #define DG_ERR_WORKSPACE 4
 #define DG_ERR_DEVICE 5
 #define DG_ERR_HIP 6
+#define DG_ERR_FORMAT 7
+
+/* 8-bit operand formats (OCP): E4M3 ("fn": bias 7, max 448, no infinities) and E5M2
+ * (bias 15, max 57344, with infinities).  The usage guide allows either for the inputs
+ * (aisharenet.com/ja usage guide, main functions, section 1). */
+#define DG_FP8_E4M3 0
+#define DG_FP8_E5M2 1
 
 #define DG_DENSE 0
 #define DG_CONTIGUOUS 1
@@ -128,6 +137,28 @@ dg_status dg_grouped_gemm_fp8_masked(const uint8_t *A, const float *sA,
                                      const int32_t *masked_m, uint16_t *C,
                                      int64_t G, int64_t cap, int64_t N, int64_t K,
                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* The same three calls with explicit operand formats: a_format / b_format are
+ * DG_FP8_E4M3 or DG_FP8_E5M2 (any pair), else DG_ERR_FORMAT.  The calls above are these
+ * with both formats DG_FP8_E4M3.  Everything else (layouts, scales, routing, workspace,
+ * errors, execution) is as described there; the choice of kernel instance, and hence
+ * dg_workspace_bytes / dg_instance_name, does not depend on the formats.
+ * (aisharenet.com/ja usage guide, main functions, section 1: E4M3 or E5M2 inputs.) */
+dg_status dg_gemm_fp8_nt_ex(const uint8_t *A, int a_format, const float *sA,
+                            const uint8_t *B, int b_format, const float *sB,
+                            uint16_t *C, int64_t M, int64_t N, int64_t K,
+                            void *workspace, size_t workspace_bytes, void *stream);
+dg_status dg_grouped_gemm_fp8_contiguous_ex(const uint8_t *A, int a_format, const float *sA,
+                                            const uint8_t *B, int b_format, const float *sB,
+                                            const int32_t *group_idx, uint16_t *C,
+                                            int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                            void *workspace, size_t workspace_bytes,
+                                            void *stream);
+dg_status dg_grouped_gemm_fp8_masked_ex(const uint8_t *A, int a_format, const float *sA,
+                                        const uint8_t *B, int b_format, const float *sB,
+                                        const int32_t *masked_m, uint16_t *C,
+                                        int64_t G, int64_t cap, int64_t N, int64_t K,
+                                        void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

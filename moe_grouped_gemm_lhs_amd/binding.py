@@ -17,6 +17,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdg.so")
 
 DG_DENSE, DG_CONTIGUOUS, DG_MASKED = 0, 1, 2
+DG_FP8_E4M3, DG_FP8_E5M2 = 0, 1
+_FORMATS = {"e4m3": DG_FP8_E4M3, "e5m2": DG_FP8_E5M2}
+_FP8_DTYPES = {torch.float8_e4m3fn: DG_FP8_E4M3, torch.float8_e5m2: DG_FP8_E5M2}
 _lib = None
 _lock = threading.Lock()
 _workspaces: dict = {}
@@ -57,6 +60,14 @@ def load_library():
         lib.dg_grouped_gemm_fp8_masked.restype = I
         lib.dg_grouped_gemm_fp8_masked.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64,
                                                    P, SZ, P]
+        lib.dg_gemm_fp8_nt_ex.restype = I
+        lib.dg_gemm_fp8_nt_ex.argtypes = [P, I, P, P, I, P, P, I64, I64, I64, P, SZ, P]
+        lib.dg_grouped_gemm_fp8_contiguous_ex.restype = I
+        lib.dg_grouped_gemm_fp8_contiguous_ex.argtypes = [P, I, P, P, I, P, P, P, I64, I64, I64,
+                                                          I64, P, SZ, P]
+        lib.dg_grouped_gemm_fp8_masked_ex.restype = I
+        lib.dg_grouped_gemm_fp8_masked_ex.argtypes = [P, I, P, P, I, P, P, P, I64, I64, I64,
+                                                      I64, P, SZ, P]
         _lib = lib
     return _lib
 
@@ -78,12 +89,20 @@ def dg_instance_name(kind: int, rows_or_cap: int, N: int, K: int, G: int = 1) ->
 
 
 # ------------------------------------------------------------------------ marshalling
-def _bytes_view(t: torch.Tensor, name: str) -> torch.Tensor:
-    if t.dtype in (torch.float8_e4m3fn,):
-        t = t.view(torch.uint8)
+def _bytes_view(t: torch.Tensor, name: str, fmt=None):
+    """The operand as uint8 bytes and its format code: float8_e4m3fn / float8_e5m2
+    tensors carry their format; uint8 bytes are E4M3 unless `fmt` ('e4m3' / 'e5m2')
+    says otherwise."""
+    if fmt is not None and fmt not in _FORMATS:
+        raise ValueError(f"{name}: unknown operand format {fmt!r}")
+    if t.dtype in _FP8_DTYPES:
+        code = _FP8_DTYPES[t.dtype]
+        if fmt is not None and _FORMATS[fmt] != code:
+            raise ValueError(f"{name}: format {fmt!r} contradicts dtype {t.dtype}")
+        return t.view(torch.uint8), code
     if t.dtype != torch.uint8:
-        raise TypeError(f"{name} must be uint8 or float8_e4m3fn, got {t.dtype}")
-    return t
+        raise TypeError(f"{name} must be uint8, float8_e4m3fn or float8_e5m2, got {t.dtype}")
+    return t, _FORMATS[fmt or "e4m3"]
 
 
 def _check(t: torch.Tensor, name: str, dtype, shape, device):
@@ -122,9 +141,12 @@ def _workspace(kind, rows, N, K, G, device, workspace):
     return ws, ws.numel()
 
 
-def dg_gemm_fp8_nt(A, sA, B, sB, C=None, *, workspace=None, stream=None):
-    """Dense C (M x N bf16) = A (M x K e4m3) x B (N x K e4m3)^T with block scales."""
-    A, B = _bytes_view(A, "A"), _bytes_view(B, "B")
+def dg_gemm_fp8_nt(A, sA, B, sB, C=None, *, a_format=None, b_format=None, workspace=None,
+                   stream=None):
+    """Dense C (M x N bf16) = A (M x K fp8) x B (N x K fp8)^T with block scales.  The
+    operand formats come from float8 dtypes, or a_format / b_format ('e4m3', 'e5m2')
+    for uint8 bytes (default E4M3); any non-E4M3 operand goes through the _ex call."""
+    (A, fa), (B, fb) = _bytes_view(A, "A", a_format), _bytes_view(B, "B", b_format)
     M, K = A.shape
     N = B.shape[0]
     dev = A.device
@@ -137,17 +159,23 @@ def dg_gemm_fp8_nt(A, sA, B, sB, C=None, *, workspace=None, stream=None):
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _check(C, "C", torch.bfloat16, (M, N), dev)
     ws, wsb = _workspace(DG_DENSE, M, N, K, 1, dev, workspace)
-    st = load_library().dg_gemm_fp8_nt(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
-                                       _ptr(ws), wsb, _stream(dev, stream))
+    lib = load_library()
+    if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3:
+        st = lib.dg_gemm_fp8_nt(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
+                                _ptr(ws), wsb, _stream(dev, stream))
+    else:
+        st = lib.dg_gemm_fp8_nt_ex(_ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), _ptr(C), M, N,
+                                   K, _ptr(ws), wsb, _stream(dev, stream))
     if st != 0:
         raise DGError(st, "dg_gemm_fp8_nt")
     return C
 
 
-def dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, group_idx, C=None, *, workspace=None,
-                                   stream=None):
-    """Contiguous grouped GEMM: A (M_total x K), B (G x N x K), group_idx (M_total int32)."""
-    A, B = _bytes_view(A, "A"), _bytes_view(B, "B")
+def dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, group_idx, C=None, *, a_format=None,
+                                   b_format=None, workspace=None, stream=None):
+    """Contiguous grouped GEMM: A (M_total x K), B (G x N x K), group_idx (M_total int32);
+    operand formats as for dg_gemm_fp8_nt."""
+    (A, fa), (B, fb) = _bytes_view(A, "A", a_format), _bytes_view(B, "B", b_format)
     M, K = A.shape
     G, N = B.shape[0], B.shape[1]
     dev = A.device
@@ -161,18 +189,25 @@ def dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, group_idx, C=None, *, workspace
         C = torch.zeros((M, N), dtype=torch.bfloat16, device=dev)
     _check(C, "C", torch.bfloat16, (M, N), dev)
     ws, wsb = _workspace(DG_CONTIGUOUS, M, N, K, G, dev, workspace)
-    st = load_library().dg_grouped_gemm_fp8_contiguous(
-        _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(group_idx), _ptr(C), M, N, K, G,
-        _ptr(ws), wsb, _stream(dev, stream))
+    lib = load_library()
+    if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3:
+        st = lib.dg_grouped_gemm_fp8_contiguous(
+            _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(group_idx), _ptr(C), M, N, K, G,
+            _ptr(ws), wsb, _stream(dev, stream))
+    else:
+        st = lib.dg_grouped_gemm_fp8_contiguous_ex(
+            _ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), _ptr(group_idx), _ptr(C), M, N, K, G,
+            _ptr(ws), wsb, _stream(dev, stream))
     if st != 0:
         raise DGError(st, "dg_grouped_gemm_fp8_contiguous")
     return C
 
 
-def dg_grouped_gemm_fp8_masked(A, sA, B, sB, masked_m, C=None, *, workspace=None,
-                               stream=None):
-    """Masked grouped GEMM: A (G x cap x K), B (G x N x K), masked_m (G int32)."""
-    A, B = _bytes_view(A, "A"), _bytes_view(B, "B")
+def dg_grouped_gemm_fp8_masked(A, sA, B, sB, masked_m, C=None, *, a_format=None,
+                               b_format=None, workspace=None, stream=None):
+    """Masked grouped GEMM: A (G x cap x K), B (G x N x K), masked_m (G int32); operand
+    formats as for dg_gemm_fp8_nt."""
+    (A, fa), (B, fb) = _bytes_view(A, "A", a_format), _bytes_view(B, "B", b_format)
     G, cap, K = A.shape
     N = B.shape[1]
     dev = A.device
@@ -186,9 +221,15 @@ def dg_grouped_gemm_fp8_masked(A, sA, B, sB, masked_m, C=None, *, workspace=None
         C = torch.zeros((G, cap, N), dtype=torch.bfloat16, device=dev)
     _check(C, "C", torch.bfloat16, (G, cap, N), dev)
     ws, wsb = _workspace(DG_MASKED, cap, N, K, G, dev, workspace)
-    st = load_library().dg_grouped_gemm_fp8_masked(
-        _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(masked_m), _ptr(C), G, cap, N, K,
-        _ptr(ws), wsb, _stream(dev, stream))
+    lib = load_library()
+    if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3:
+        st = lib.dg_grouped_gemm_fp8_masked(
+            _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(masked_m), _ptr(C), G, cap, N, K,
+            _ptr(ws), wsb, _stream(dev, stream))
+    else:
+        st = lib.dg_grouped_gemm_fp8_masked_ex(
+            _ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), _ptr(masked_m), _ptr(C), G, cap, N,
+            K, _ptr(ws), wsb, _stream(dev, stream))
     if st != 0:
         raise DGError(st, "dg_grouped_gemm_fp8_masked")
     return C

@@ -77,13 +77,17 @@ dg_status check_shape(int kind, int64_t rows_or_cap, int64_t N, int64_t K, int64
   return DG_OK;
 }
 
-const Instance* find_instance(const char* name) {
+// The instance of that name built for these operand formats.
+const Instance* find_instance(const char* name, int fa = dg::kFmtE4M3, int fb = dg::kFmtE4M3) {
   int n = 0;
   const Instance* all = dg::instances(&n);
   for (int i = 0; i < n; ++i)
-    if (strcmp(all[i].name, name) == 0) return &all[i];
+    if (strcmp(all[i].name, name) == 0 && all[i].fmt_a == fa && all[i].fmt_b == fb)
+      return &all[i];
   return nullptr;
 }
+
+bool valid_format(int f) { return f == DG_FP8_E4M3 || f == DG_FP8_E5M2; }
 
 constexpr int kAssumedCUs = 256;   // MI355X; selection is host-only and device-free
 
@@ -105,11 +109,13 @@ bool stream_fits(const Instance* in, int64_t rows, int64_t N) {
 
 // Instance selection: the heuristic that maps a problem to a build-time instance.
 // DG_FORCE_INSTANCE=<name> overrides it when the named instance serves the call kind.
+// Every tile shape is built for all four operand-format pairs, so the choice of shape
+// does not depend on the formats; `fa` / `fb` only pick that shape's build.
 const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_t K,
-                                int64_t G) {
+                                int64_t G, int fa = dg::kFmtE4M3, int fb = dg::kFmtE4M3) {
   const char* forced = getenv("DG_FORCE_INSTANCE");
   if (forced && *forced) {
-    const Instance* f = find_instance(forced);
+    const Instance* f = find_instance(forced, fa, fb);
     if (f && f->kind == kind && stream_fits(f, rows_or_cap, N)) return f;
   }
   const char* name = nullptr;
@@ -139,11 +145,11 @@ const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_
       static char buf[64];
       for (const Opt& o : opts) {
         snprintf(buf, sizeof(buf), "%s_%s", pre, o.suffix);
-        if (!find_instance(buf)) continue;
+        if (!find_instance(buf, fa, fb)) continue;
         const double c = tile_cost(rows_or_cap, N, groups, o.bm, o.bn, o.eff);
         if (c < best) {
           best = c;
-          name = find_instance(buf)->name;
+          name = find_instance(buf, fa, fb)->name;
         }
       }
       if (kind == dg::kMasked && rows_or_cap <= 64) name = "masked_64x128";
@@ -152,7 +158,7 @@ const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_
     default:
       return nullptr;
   }
-  return name ? find_instance(name) : nullptr;
+  return name ? find_instance(name, fa, fb) : nullptr;
 }
 
 void fill_tiles(GemmArgs& a, const Instance* in, int kind) {
@@ -171,8 +177,9 @@ size_t workspace_for(const Instance* in, const GemmArgs& a) {
   return 0;
 }
 
-dg_status run(int kind, GemmArgs& a, void* workspace, size_t workspace_bytes, void* stream) {
-  const Instance* in = select_instance(kind, a.rows, a.N, a.K, a.G);
+dg_status run(int kind, int fa, int fb, GemmArgs& a, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  const Instance* in = select_instance(kind, a.rows, a.N, a.K, a.G, fa, fb);
   if (!in) return DG_ERR_SHAPE;
   fill_tiles(a, in, kind);
   const size_t ws = workspace_for(in, a);
@@ -187,8 +194,8 @@ dg_status run(int kind, GemmArgs& a, void* workspace, size_t workspace_bytes, vo
   if (st != DG_OK) return st;
   const int grid = in->grid(a, num_cus);
   if (log_enabled())
-    fprintf(stderr, "[dg] kind=%d rows=%d N=%d K=%d G=%d -> %s grid=%d\n", kind, a.rows, a.N,
-            a.K, a.G, in->name, grid);
+    fprintf(stderr, "[dg] kind=%d fmt=%d/%d rows=%d N=%d K=%d G=%d -> %s grid=%d\n", kind, fa,
+            fb, a.rows, a.N, a.K, a.G, in->name, grid);
   if (grid <= 0) return DG_OK;
   (void)hipGetLastError();
   in->launch(a, grid, (hipStream_t)stream);
@@ -211,6 +218,7 @@ const char* dg_status_string(dg_status s) {
     case DG_ERR_WORKSPACE: return "DG_ERR_WORKSPACE";
     case DG_ERR_DEVICE: return "DG_ERR_DEVICE";
     case DG_ERR_HIP: return "DG_ERR_HIP";
+    case DG_ERR_FORMAT: return "DG_ERR_FORMAT";
     default: return "DG_ERR_UNKNOWN";
   }
 }
@@ -241,11 +249,12 @@ const char* dg_instance_name(int kind, int64_t rows_or_cap, int64_t N, int64_t K
   return in ? in->name : "none";
 }
 
-dg_status dg_gemm_fp8_nt(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
-                         uint16_t* C, int64_t M, int64_t N, int64_t K, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+dg_status dg_gemm_fp8_nt_ex(const uint8_t* A, int a_format, const float* sA, const uint8_t* B,
+                            int b_format, const float* sB, uint16_t* C, int64_t M, int64_t N,
+                            int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   dg_status st = check_shape(dg::kDense, M, N, K, 1);
   if (st != DG_OK) return st;
+  if (!valid_format(a_format) || !valid_format(b_format)) return DG_ERR_FORMAT;
   if (M == 0 || N == 0) return DG_OK;
   if (!A || !sA || !B || !sB || !C) return DG_ERR_NULL;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(sA, 4) ||
@@ -254,16 +263,25 @@ dg_status dg_gemm_fp8_nt(const uint8_t* A, const float* sA, const uint8_t* B, co
   GemmArgs a{};
   a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C;
   a.rows = (int)M; a.N = (int)N; a.K = (int)K; a.G = 1;
-  return run(dg::kDense, a, workspace, workspace_bytes, stream);
+  return run(dg::kDense, a_format, b_format, a, workspace, workspace_bytes, stream);
 }
 
-dg_status dg_grouped_gemm_fp8_contiguous(const uint8_t* A, const float* sA, const uint8_t* B,
-                                         const float* sB, const int32_t* group_idx,
-                                         uint16_t* C, int64_t M_total, int64_t N, int64_t K,
-                                         int64_t G, void* workspace, size_t workspace_bytes,
-                                         void* stream) {
+dg_status dg_gemm_fp8_nt(const uint8_t* A, const float* sA, const uint8_t* B, const float* sB,
+                         uint16_t* C, int64_t M, int64_t N, int64_t K, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return dg_gemm_fp8_nt_ex(A, DG_FP8_E4M3, sA, B, DG_FP8_E4M3, sB, C, M, N, K, workspace,
+                           workspace_bytes, stream);
+}
+
+dg_status dg_grouped_gemm_fp8_contiguous_ex(const uint8_t* A, int a_format, const float* sA,
+                                            const uint8_t* B, int b_format, const float* sB,
+                                            const int32_t* group_idx, uint16_t* C,
+                                            int64_t M_total, int64_t N, int64_t K, int64_t G,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream) {
   dg_status st = check_shape(dg::kContiguous, M_total, N, K, G);
   if (st != DG_OK) return st;
+  if (!valid_format(a_format) || !valid_format(b_format)) return DG_ERR_FORMAT;
   if (M_total == 0 || N == 0) return DG_OK;
   if (!A || !sA || !B || !sB || !group_idx || !C) return DG_ERR_NULL;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(sA, 4) ||
@@ -272,15 +290,27 @@ dg_status dg_grouped_gemm_fp8_contiguous(const uint8_t* A, const float* sA, cons
   GemmArgs a{};
   a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C; a.group_idx = group_idx;
   a.rows = (int)M_total; a.N = (int)N; a.K = (int)K; a.G = (int)G;
-  return run(dg::kContiguous, a, workspace, workspace_bytes, stream);
+  return run(dg::kContiguous, a_format, b_format, a, workspace, workspace_bytes, stream);
 }
 
-dg_status dg_grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const uint8_t* B,
-                                     const float* sB, const int32_t* masked_m, uint16_t* C,
-                                     int64_t G, int64_t cap, int64_t N, int64_t K,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+dg_status dg_grouped_gemm_fp8_contiguous(const uint8_t* A, const float* sA, const uint8_t* B,
+                                         const float* sB, const int32_t* group_idx,
+                                         uint16_t* C, int64_t M_total, int64_t N, int64_t K,
+                                         int64_t G, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  return dg_grouped_gemm_fp8_contiguous_ex(A, DG_FP8_E4M3, sA, B, DG_FP8_E4M3, sB, group_idx,
+                                           C, M_total, N, K, G, workspace, workspace_bytes,
+                                           stream);
+}
+
+dg_status dg_grouped_gemm_fp8_masked_ex(const uint8_t* A, int a_format, const float* sA,
+                                        const uint8_t* B, int b_format, const float* sB,
+                                        const int32_t* masked_m, uint16_t* C, int64_t G,
+                                        int64_t cap, int64_t N, int64_t K, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
   dg_status st = check_shape(dg::kMasked, cap, N, K, G);
   if (st != DG_OK) return st;
+  if (!valid_format(a_format) || !valid_format(b_format)) return DG_ERR_FORMAT;
   if (cap == 0 || N == 0) return DG_OK;
   if (!A || !sA || !B || !sB || !masked_m || !C) return DG_ERR_NULL;
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(sA, 4) ||
@@ -289,7 +319,15 @@ dg_status dg_grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const ui
   GemmArgs a{};
   a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C; a.masked_m = masked_m;
   a.rows = (int)cap; a.N = (int)N; a.K = (int)K; a.G = (int)G;
-  return run(dg::kMasked, a, workspace, workspace_bytes, stream);
+  return run(dg::kMasked, a_format, b_format, a, workspace, workspace_bytes, stream);
+}
+
+dg_status dg_grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const uint8_t* B,
+                                     const float* sB, const int32_t* masked_m, uint16_t* C,
+                                     int64_t G, int64_t cap, int64_t N, int64_t K,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return dg_grouped_gemm_fp8_masked_ex(A, DG_FP8_E4M3, sA, B, DG_FP8_E4M3, sB, masked_m, C, G,
+                                       cap, N, K, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

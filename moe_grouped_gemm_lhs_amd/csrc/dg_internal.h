@@ -25,6 +25,7 @@ constexpr int kModeTiled = 0;    // one output tile per work item
 constexpr int kModeStream = 2;   // persistent stream-K over (tile, K block) iterations
 
 enum Kind : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+enum Fmt : int { kFmtE4M3 = 0, kFmtE5M2 = 1 };
 
 // Everything a kernel needs to know about one call.
 struct GemmArgs {
@@ -53,6 +54,7 @@ struct Instance {
   int bm, bn;        // output tile
   int mode;          // kModeTiled or kModeStream
   int threads;       // workgroup size
+  int fmt_a, fmt_b;  // operand formats (kFmtE4M3 / kFmtE5M2)
   // grid size for a call (0 = nothing to launch)
   int (*grid)(const GemmArgs& a, int num_cus);
   void (*launch)(const GemmArgs& a, int grid, hipStream_t stream);

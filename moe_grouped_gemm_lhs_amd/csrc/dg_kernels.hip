@@ -45,10 +45,13 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Format codes of the f8f6f4 MFMA operands: 0 = E4M3, 1 = E5M2 (the values of
+// DG_FP8_E4M3 / DG_FP8_E5M2).  FA is the format of the instruction's first operand,
+// FB of its second; the scale operands are 0 (no hardware block scaling).
+template <int FA, int FB>
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  // format codes 0/0: both operands e4m3; scale operands 0: no hardware block scaling.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, FA, FB, 0, 0, 0, 0);
 }
 
 // s_waitcnt with only the vector-memory counter constrained (expcnt/lgkmcnt untouched).
@@ -131,12 +134,14 @@ __device__ __forceinline__ void stage_barrier() {
 
 // Compile-time shape of one kernel instance.
 // B_NT: B blocks are read by exactly one workgroup (decode shapes), so they are loaded
-// non-temporal.
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, bool B_NT_ = false>
+// non-temporal.  FMT_A / FMT_B: operand formats (0: E4M3, 1: E5M2).
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, bool B_NT_ = false,
+          int FMT_A_ = 0, int FMT_B_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int STAGES = STAGES_;
   static constexpr bool B_NT = B_NT_;
+  static constexpr int FMT_A = FMT_A_, FMT_B = FMT_B_;
   static constexpr int W = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * W;
   static constexpr int WM = BM / WAVES_M;       // rows per wave
@@ -318,7 +323,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* __restrict__ st, co
     if (t < T) {
       const int j = t / TI, i = t % TI;
       if (i == 0 && j + 1 < TJ) bf[(j + 1) & 1] = read_frag(Bs, c.wn * WN + 16 * (j + 1) + l16, q);
-      part[t] = mfma_fp8_16x16x128(bf[j & 1], af[i]);
+      part[t] = mfma_fp8_16x16x128<C::FMT_B, C::FMT_A>(bf[j & 1], af[i]);   // B first
     }
     if (t >= 2) {
       const int u = t - 2;
@@ -740,23 +745,33 @@ int grid_persistent(const GemmArgs& a, int num_cus) {
   return a.num_tiles < num_cus ? a.num_tiles : num_cus;
 }
 
-using Big = Cfg<256, 256, 4, 2, 2>;      // 8 waves, 64x128 per wave
-using Big224 = Cfg<256, 224, 4, 2, 2>;   // non-power-of-two columns: 64x112 per wave
-using Mid = Cfg<128, 128, 2, 2, 3>;      // 4 waves, 64x64 per wave
-using Small = Cfg<64, 128, 1, 4, 4>;     // 4 waves, 64x32 per wave, 4 stages
+// Tile shapes, each built for the four operand-format pairs (FA, FB).
+template <int FA, int FB> using Big = Cfg<256, 256, 4, 2, 2, false, FA, FB>;     // 8 waves, 64x128 each
+template <int FA, int FB> using Big224 = Cfg<256, 224, 4, 2, 2, false, FA, FB>;  // non-power-of-two N tile
+template <int FA, int FB> using Mid = Cfg<128, 128, 2, 2, 3, false, FA, FB>;     // 4 waves, 64x64 each
+template <int FA, int FB> using Small = Cfg<64, 128, 1, 4, 4, false, FA, FB>;    // 4 waves, 64x32 each
 // stream-K decode instances: 8 waves (a wave's direct-to-LDS copies are issue-bound, so
 // a workgroup needs eight of them to draw its share of HBM bandwidth), B non-temporal
-using Str64 = Cfg<64, 128, 2, 4, 5, true>;     // 64 rows x 128 columns
-using Str64n64 = Cfg<64, 64, 2, 4, 8, true>;   // 64 rows x 64 columns
-using Str128 = Cfg<128, 128, 2, 4, 4, true>;   // 128 rows x 128 columns
-using Str128n64 = Cfg<128, 64, 2, 4, 6, true>; // 128 rows x 64 columns
+template <int FA, int FB> using Str64 = Cfg<64, 128, 2, 4, 5, true, FA, FB>;     // 64 rows x 128 columns
+template <int FA, int FB> using Str64n64 = Cfg<64, 64, 2, 4, 8, true, FA, FB>;   // 64 rows x 64 columns
+template <int FA, int FB> using Str128 = Cfg<128, 128, 2, 4, 4, true, FA, FB>;   // 128 rows x 128 columns
+template <int FA, int FB> using Str128n64 = Cfg<128, 64, 2, 4, 6, true, FA, FB>; // 128 rows x 64 columns
 
 }  // namespace
 
-#define DG_INST(NAME, KIND, C) \
-  Instance { NAME, KIND, C::BM, C::BN, kModeTiled, C::NT, grid_persistent, launch<KIND, C> }
-#define DG_STREAM(NAME, C) \
-  Instance { NAME, kDense, C::BM, C::BN, kModeStream, C::NT, grid_stream, launch_stream<C> }
+#define DG_INST1(NAME, KIND, C, FA, FB)                                                   \
+  Instance { NAME, KIND, C::BM, C::BN, kModeTiled, C::NT, FA, FB, grid_persistent,        \
+             launch<KIND, C> }
+#define DG_STREAM1(NAME, C, FA, FB)                                                        \
+  Instance { NAME, kDense, C::BM, C::BN, kModeStream, C::NT, FA, FB, grid_stream,         \
+             launch_stream<C> }
+#define DG_INST(NAME, KIND, T)                                                             \
+  DG_INST1(NAME, KIND, T<0 COMMA 0>, 0, 0), DG_INST1(NAME, KIND, T<1 COMMA 1>, 1, 1),      \
+      DG_INST1(NAME, KIND, T<0 COMMA 1>, 0, 1), DG_INST1(NAME, KIND, T<1 COMMA 0>, 1, 0)
+#define DG_STREAM(NAME, T)                                                                 \
+  DG_STREAM1(NAME, T<0 COMMA 0>, 0, 0), DG_STREAM1(NAME, T<1 COMMA 1>, 1, 1),              \
+      DG_STREAM1(NAME, T<0 COMMA 1>, 0, 1), DG_STREAM1(NAME, T<1 COMMA 0>, 1, 0)
+#define COMMA ,
 
 static const Instance kInstances[] = {
     DG_INST("dense_256x256", kDense, Big),

@@ -45,15 +45,17 @@ def run_gpu(p, c_init_bits=None, group_idx=None, masked_m=None, ops=None, worksp
     if c_init_bits is None:
         c_init_bits = np.full(out_shape(p), SENTINEL, np.uint16)
     C = torch.from_numpy(c_init_bits.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    fm = dict(a_format=p.a_fmt, b_format=p.b_fmt)
     if p.kind == "dense":
-        dg.dg_gemm_fp8_nt(A, sA, B, sB, C, workspace=workspace)
+        dg.dg_gemm_fp8_nt(A, sA, B, sB, C, workspace=workspace, **fm)
     elif p.kind == "contiguous":
         gi = group_idx if group_idx is not None else p.group_idx
-        dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, torch.from_numpy(gi).to(DEV), C)
+        dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, torch.from_numpy(gi).to(DEV), C, **fm)
     else:
         mm = masked_m if masked_m is not None else p.masked_m
         Cv = C.view(p.G, p.M, p.N)
-        dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, torch.from_numpy(np.asarray(mm, np.int32)).to(DEV), Cv)
+        dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, torch.from_numpy(np.asarray(mm, np.int32)).to(DEV), Cv,
+                                      **fm)
     torch.cuda.synchronize()
     return C.view(torch.int16).cpu().numpy().view(np.uint16).reshape(out_shape(p))
 
@@ -87,7 +89,7 @@ def oracle_rows(p, rows, group_idx=None):
         r = rows[sel]
         Bg = p.B[g * p.N:(g + 1) * p.N]
         sBg = p.sB[g * nnb:(g + 1) * nnb]
-        out[sel] = oracle.gemm_fp8_nt(p.A[r], p.sA[r], Bg, sBg)
+        out[sel] = oracle.gemm_fp8_nt(p.A[r], p.sA[r], Bg, sBg, a_fmt=p.a_fmt, b_fmt=p.b_fmt)
     return out
 
 
@@ -95,14 +97,16 @@ def oracle_full(p, c_init_bits=None, group_idx=None, masked_m=None):
     if c_init_bits is None:
         c_init_bits = np.full(out_shape(p), SENTINEL, np.uint16)
     C = c_init_bits.copy()
+    fm = dict(a_fmt=p.a_fmt, b_fmt=p.b_fmt)
     if p.kind == "dense":
-        oracle.gemm_fp8_nt(p.A, p.sA, p.B, p.sB, C=C)
+        oracle.gemm_fp8_nt(p.A, p.sA, p.B, p.sB, C=C, **fm)
     elif p.kind == "contiguous":
         gi = group_idx if group_idx is not None else p.group_idx
-        oracle.grouped_contiguous(p.A, p.sA, p.B, p.sB, gi, p.G, C=C)
+        oracle.grouped_contiguous(p.A, p.sA, p.B, p.sB, gi, p.G, C=C, **fm)
     else:
         mm = masked_m if masked_m is not None else p.masked_m
-        oracle.grouped_masked(p.A, p.sA, p.B, p.sB, np.asarray(mm, np.int32), p.G, p.M, C=C)
+        oracle.grouped_masked(p.A, p.sA, p.B, p.sB, np.asarray(mm, np.int32), p.G, p.M, C=C,
+                              **fm)
     return C
 
 

@@ -40,8 +40,8 @@ def test_constants_and_strings(lib):
     from moe_grouped_gemm_lhs_amd import binding as b
     assert b.dg_get_m_alignment_for_contiguous_layout() == 128
     want = ["DG_OK", "DG_ERR_NULL", "DG_ERR_SHAPE", "DG_ERR_ALIGN", "DG_ERR_WORKSPACE",
-            "DG_ERR_DEVICE", "DG_ERR_HIP"]
-    assert [b.dg_status_string(i) for i in range(7)] == want
+            "DG_ERR_DEVICE", "DG_ERR_HIP", "DG_ERR_FORMAT"]
+    assert [b.dg_status_string(i) for i in range(8)] == want
     assert b.dg_status_string(99) == "DG_ERR_UNKNOWN"
 
 
@@ -67,6 +67,25 @@ def test_dense_validation_codes(lib):
     assert dense(lib, C=A16 + 2) == 3
     assert dense(lib, sA=A4 + 1) == 3
     assert dense(lib, M=1 << 31) == 2
+
+
+def test_format_validation_codes(lib):
+    f = lib.dg_gemm_fp8_nt_ex
+    # formats are checked right after the shapes, before the empty-output shortcut
+    assert f(A16, 2, A4, A16, 0, A4, A16, 64, 256, 512, None, 0, None) == 7
+    assert f(A16, 0, A4, A16, -1, A4, A16, 64, 256, 512, None, 0, None) == 7
+    assert f(A16, 5, A4, A16, 0, A4, A16, 0, 256, 512, None, 0, None) == 7
+    assert f(A16, 5, A4, A16, 0, A4, A16, 64, 256, 100, None, 0, None) == 2    # shape first
+    for fa in (0, 1):
+        for fb in (0, 1):
+            assert f(A16, fa, A4, A16, fb, A4, A16, 0, 256, 512, None, 0, None) == 0
+            assert f(None, fa, A4, A16, fb, A4, A16, 64, 256, 512, None, 0, None) == 1
+    c = lib.dg_grouped_gemm_fp8_contiguous_ex
+    assert c(A16, 0, A4, A16, 3, A4, A4, A16, 256, 128, 128, 2, None, 0, None) == 7
+    assert c(A16, 1, A4, A16, 1, A4, None, A16, 256, 128, 128, 2, None, 0, None) == 1
+    m = lib.dg_grouped_gemm_fp8_masked_ex
+    assert m(A16, 7, A4, A16, 0, A4, A4, A16, 2, 64, 128, 128, None, 0, None) == 7
+    assert m(A16, 1, A4, A16, 0, A4, None, A16, 2, 64, 128, 128, None, 0, None) == 1
 
 
 def test_grouped_validation_codes(lib):

@@ -13,7 +13,7 @@ import pytest
 
 from moe_grouped_gemm_lhs_amd import inputs as I
 from tests.helpers import (SENTINEL, assert_within_tolerance, bf16_to_f64, e4m3_codes_of,
-                           read_sections)
+                           fp8_codes_of, read_sections)
 
 pytestmark = pytest.mark.gpu
 
@@ -123,6 +123,60 @@ def test_stream_k_shared_tiles(M, N, K, monkeypatch):
             assert_within_tolerance(c_gpu, c_ref, written, f"{name} {M}x{N}x{K}")
             assert not ws.cpu().numpy().any(), f"{name}: workspace not left zero filled"
     monkeypatch.delenv("DG_FORCE_INSTANCE")
+
+
+# ------------------------------------------------------- E5M2 operands (either or both)
+FMT_PAIRS = [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")]
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", FMT_PAIRS)
+def test_formats_every_form(a_fmt, b_fmt):
+    """E5M2 for either or both operands, in every form: a decode shape (stream-K), a
+    ragged tiled dense shape, contiguous and masked grouped shapes."""
+    fm = dict(a_fmt=a_fmt, b_fmt=b_fmt)
+    cases = [I.make_dense(64, 600, 1024, seed=60, **fm),
+             I.make_dense(300, 520, 640, seed=61, outliers=True, **fm),
+             I.make_contiguous([256, 128, 384], 400, 384, seed=62, **fm),
+             I.make_masked(3, 200, 400, 384, seed=63, masked_m=[200, 37, 0], **fm)]
+    for p in cases:
+        check_full(p, f"{p.kind} {p.rows}x{p.N}x{p.K} {a_fmt}x{b_fmt}")
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", FMT_PAIRS)
+def test_formats_every_instance(a_fmt, b_fmt, monkeypatch):
+    """Each dense instance forced with E5M2 operands."""
+    from moe_grouped_gemm_lhs_amd import binding as b
+    for name in ["dense_256x256", "dense_256x224", "dense_128x128", "dense_64x128_stream",
+                 "dense_64x64_stream", "dense_128x128_stream", "dense_128x64_stream"]:
+        monkeypatch.setenv("DG_FORCE_INSTANCE", name)
+        M = 333 if "stream" not in name else (50 if name.startswith("dense_64x") else 100)
+        assert b.dg_instance_name(0, M, 400, 512, 1) == name
+        p = I.make_dense(M, 400, 512, seed=64, a_fmt=a_fmt, b_fmt=b_fmt)
+        check_full(p, f"dense forced {name} {a_fmt}x{b_fmt}")
+    monkeypatch.delenv("DG_FORCE_INSTANCE")
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", FMT_PAIRS)
+def test_formats_integer_inputs_bit_exact(a_fmt, b_fmt):
+    rng = np.random.default_rng(41)
+    M, N, K = 130, 300, 384
+    a = np.zeros((M, K))
+    for r in range(M):
+        pos = rng.choice(K, 8, replace=False)
+        a[r, pos] = rng.integers(-4, 5, 8)
+    b = rng.integers(-4, 5, (N, K)).astype(np.float64)
+    ref = (a.astype(np.int64) @ b.astype(np.int64).T).astype(np.float64)
+    p = I.Problem("dense", M, N, K, 1, fp8_codes_of(a, a_fmt), np.ones((M, 3), np.float32),
+                  fp8_codes_of(b, b_fmt), np.ones((3, 3), np.float32), a_fmt=a_fmt,
+                  b_fmt=b_fmt)
+    gu.say(f"[case] integer dense {a_fmt}x{b_fmt}")
+    assert np.array_equal(bf16_to_f64(gu.run_gpu(p)), ref)
+
+
+def test_formats_decode_shape_full():
+    case = dict(I.decode_cases()[3], a_fmt="e5m2", b_fmt="e5m2")   # 64x7168x16384
+    p = I.make(case)
+    check_sampled(p, I.case_name(case))
 
 
 def test_integer_inputs_bit_exact():
