@@ -53,6 +53,11 @@ def _load():
         lib.dgref_bf16_rne_array.argtypes = [P, P, I64]
         lib.dgref_e4m3fn_decode_array.argtypes = [P, P, I64]
         lib.dgref_e5m2_decode_array.argtypes = [P, P, I64]
+        lib.dgref_encode_fp8_array.argtypes = [P, P, I64, I]
+        lib.dgref_quantize_1x128.restype = I
+        lib.dgref_quantize_1x128.argtypes = [P, I64, I64, I, P, P]
+        lib.dgref_quantize_128x128.restype = I
+        lib.dgref_quantize_128x128.argtypes = [P, I64, I64, I, P, P]
         _lib = lib
     return _lib
 
@@ -160,3 +165,43 @@ def grouped_masked(A, sA, B, sB, masked_m, G, cap, C=None, want_acc=False, a_fmt
     _load().dgref_grouped_masked_fmt(_p(A), _fmt(a_fmt), _p(sA), _p(B), _fmt(b_fmt), _p(sB),
                                      _p(mm), _p(C), _p(acc), G, cap, N, K)
     return (C, acc) if want_acc else C
+
+
+def encode_fp8(x, fmt: str = "e4m3") -> np.ndarray:
+    """Nearest fp8 code of each (finite) value, ties to even, saturating."""
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().dgref_encode_fp8_array(_p(x), _p(out), x.size, _fmt(fmt))
+    return out
+
+
+def _as_f32(X):
+    """fp32 values of an fp32 array, or of bf16 bit patterns (uint16), exactly."""
+    X = np.asarray(X)
+    if X.dtype == np.uint16:
+        return np.ascontiguousarray((X.astype(np.uint32) << 16).view(np.float32))
+    return _c(X, np.float32)
+
+
+def quantize_1x128(X, fmt: str = "e4m3"):
+    """Per-row 1x128 quantisation of rows x K values (fp32, or bf16 bits as uint16).
+    Returns (codes uint8 rows x K, scales f32 rows x K/128)."""
+    X = _as_f32(X)
+    rows, K = X.shape
+    Q = np.empty((rows, K), np.uint8)
+    S = np.empty((rows, K // 128), np.float32)
+    if _load().dgref_quantize_1x128(_p(X), rows, K, _fmt(fmt), _p(Q), _p(S)) != 0:
+        raise ValueError("K must be a multiple of 128")
+    return Q, S
+
+
+def quantize_128x128(X, fmt: str = "e4m3"):
+    """128x128-block quantisation of rows x K values (fp32, or bf16 bits as uint16).
+    Returns (codes uint8 rows x K, scales f32 ceil(rows/128) x K/128)."""
+    X = _as_f32(X)
+    rows, K = X.shape
+    Q = np.empty((rows, K), np.uint8)
+    S = np.empty((-(-rows // 128), K // 128), np.float32)
+    if _load().dgref_quantize_128x128(_p(X), rows, K, _fmt(fmt), _p(Q), _p(S)) != 0:
+        raise ValueError("K must be a multiple of 128")
+    return Q, S

@@ -49,7 +49,8 @@
  *
  * Parity pins live in tests/ (worked example, exact-rational brute force, integer
  * inputs, power-of-two scaling, group-order independence, untouched masked rows,
- * reductions between the three forms, NumPy fp64 matmul with unit scales).
+ * reductions between the three forms, NumPy fp64 matmul with unit scales; for the
+ * quantiser, torch's fp8 rounding and the scale's definition).
  */
 #include <math.h>
 #include <stdint.h>
@@ -335,6 +336,105 @@ void dgref_grouped_masked(const uint8_t *A, const float *sA, const uint8_t *B,
                              N, K);
 }
 
+/* ------------------------------------------------------------------------------------
+ * Quantisation to fp8 with block scales -- the casting step the turtlesai.it summary
+ * (technical paragraph) leaves to the user, in the two block shapes of the method's
+ * fine-grained scaling: one scale per 1x128 block (activations, per row and K block)
+ * and one per 128x128 block (weights).  Per block: amax = max |x| in fp32; scale =
+ * amax / FMAX in fp32 (FMAX = 448 for E4M3, 57344 for E5M2; 1 when amax is 0); each
+ * code is the nearest fp8 value to x / scale (an fp32 division), ties to the even code,
+ * after saturating to +-FMAX.  Inputs are finite.  K is a multiple of 128; the row
+ * count of the 128x128 form need not be (the last block row holds the rows that exist).
+ */
+
+/* The finite fp8 code nearest to v (saturated to the largest finite value), ties to
+ * the code with an even mantissa: a search over every positive finite code. */
+static uint8_t encode_fp8_nearest(double v, int fmt)
+{
+    double maxv = fmt == DGREF_E5M2 ? 57344.0 : 448.0;
+    double a = fabs(v), best_d = INFINITY;
+    int c, best = 0;
+    if (a > maxv)
+        a = maxv;
+    for (c = 0; c < 128; ++c) {
+        double d = g_dec[fmt][c], diff;
+        if (!isfinite(d))
+            continue;
+        diff = fabs(a - d);
+        if (diff < best_d || (diff == best_d && (c & 1) == 0)) {
+            best_d = diff;
+            best = c;
+        }
+    }
+    if (signbit(v))
+        best |= 0x80;
+    return (uint8_t)best;
+}
+
+static float block_scale(float amax, int fmt)
+{
+    float fmax = fmt == DGREF_E5M2 ? 57344.0f : 448.0f;
+    return amax == 0.0f ? 1.0f : amax / fmax;
+}
+
+/* X rows x K fp32 -> Q rows x K codes, S rows x K/128 scales.  Returns -1 for an
+ * unknown format or K not a multiple of 128, else 0. */
+int dgref_quantize_1x128(const float *X, int64_t rows, int64_t K, int fmt, uint8_t *Q,
+                         float *S)
+{
+    int64_t nkb = K / DGREF_BLOCK, r;
+    if ((fmt != DGREF_E4M3 && fmt != DGREF_E5M2) || K % DGREF_BLOCK != 0)
+        return -1;
+    build_decode_table();
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        int64_t kb, k;
+        for (kb = 0; kb < nkb; ++kb) {
+            const float *x = X + r * K + kb * DGREF_BLOCK;
+            float amax = 0.0f, scale;
+            for (k = 0; k < DGREF_BLOCK; ++k)
+                if (fabsf(x[k]) > amax)
+                    amax = fabsf(x[k]);
+            scale = block_scale(amax, fmt);
+            S[r * nkb + kb] = scale;
+            for (k = 0; k < DGREF_BLOCK; ++k) {
+                float q = x[k] / scale;
+                Q[r * K + kb * DGREF_BLOCK + k] = encode_fp8_nearest((double)q, fmt);
+            }
+        }
+    }
+    return 0;
+}
+
+/* X rows x K fp32 -> Q rows x K codes, S ceil(rows/128) x K/128 scales. */
+int dgref_quantize_128x128(const float *X, int64_t rows, int64_t K, int fmt, uint8_t *Q,
+                           float *S)
+{
+    int64_t nkb = K / DGREF_BLOCK, nrb = (rows + DGREF_BLOCK - 1) / DGREF_BLOCK, b;
+    if ((fmt != DGREF_E4M3 && fmt != DGREF_E5M2) || K % DGREF_BLOCK != 0)
+        return -1;
+    build_decode_table();
+#pragma omp parallel for schedule(static)
+    for (b = 0; b < nrb * nkb; ++b) {
+        int64_t rb = b / nkb, kb = b % nkb, r, k;
+        int64_t r0 = rb * DGREF_BLOCK, r1 = r0 + DGREF_BLOCK < rows ? r0 + DGREF_BLOCK : rows;
+        int64_t k0 = kb * DGREF_BLOCK;
+        float amax = 0.0f, scale;
+        for (r = r0; r < r1; ++r)
+            for (k = k0; k < k0 + DGREF_BLOCK; ++k)
+                if (fabsf(X[r * K + k]) > amax)
+                    amax = fabsf(X[r * K + k]);
+        scale = block_scale(amax, fmt);
+        S[rb * nkb + kb] = scale;
+        for (r = r0; r < r1; ++r)
+            for (k = k0; k < k0 + DGREF_BLOCK; ++k) {
+                float q = X[r * K + k] / scale;
+                Q[r * K + k] = encode_fp8_nearest((double)q, fmt);
+            }
+    }
+    return 0;
+}
+
 /* Element-wise helpers for the tests. */
 void dgref_bf16_rne_array(const double *x, uint16_t *out, int64_t n)
 {
@@ -355,4 +455,13 @@ void dgref_e5m2_decode_array(const uint8_t *codes, double *out, int64_t n)
     int64_t i;
     for (i = 0; i < n; ++i)
         out[i] = dgref_e5m2_decode(codes[i]);
+}
+
+/* fp8 encoding (nearest, ties to even, saturating) of each value, for the tests. */
+void dgref_encode_fp8_array(const double *x, uint8_t *out, int64_t n, int fmt)
+{
+    int64_t i;
+    build_decode_table();
+    for (i = 0; i < n; ++i)
+        out[i] = encode_fp8_nearest(x[i], fmt);
 }
