@@ -31,7 +31,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "contiguous", "masked", "small"])
+                    choices=["decode", "prefill", "contiguous", "masked", "small", "quant"])
     ap.add_argument("--shapes", default="", help="comma-separated subset of shape indices")
     ap.add_argument("--formats", default="e4m3xe4m3",
                     choices=["e4m3xe4m3", "e5m2xe5m2", "e4m3xe5m2", "e5m2xe4m3"],
@@ -50,7 +50,14 @@ def workload_cases(name):
             "small": I.small_case}[name]()
 
 
+# fp8 block quantisation: (block shape, rows, K) of bf16 inputs -- the activations of the
+# prefill and decode shapes (1x128 per token) and two weight matrices (128x128 blocks)
+QUANT_CASES = [("1x128", 4096, 7168), ("1x128", 128, 7168), ("128x128", 7168, 16384),
+               ("128x128", 24576, 1536)]
+
 WORKLOAD_TEXT = {
+    "quant": "fp8 block quantisation of bf16 inputs: 1x128 for 4096x7168 and 128x7168 "
+             "activations, 128x128 for 7168x16384 and 24576x1536 weights",
     "decode": "dense decode FP8 NT GEMM, M in {64,128} x (N,K) in {(2112,7168),(24576,1536),"
               "(32768,512),(7168,16384),(4096,7168),(7168,2048)}, 12 shapes",
     "prefill": "dense prefill FP8 NT GEMM, M=4096 x the six (N,K) pairs, 1% N(0,30) outliers",
@@ -91,6 +98,8 @@ def main():
     torch.cuda.set_device(dev)
     dg.load_library()
 
+    if args.workload == "quant":
+        return bench_quant(args, torch, np, dg, I, dev)
     cases = workload_cases(args.workload)
     a_fmt, b_fmt = args.formats.split("x")
     if (a_fmt, b_fmt) != ("e4m3", "e4m3"):
@@ -261,6 +270,93 @@ def main():
     if args.detail:
         with open(args.detail, "w") as f:
             json.dump(dict(line=line, per_shape=per), f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+def bench_quant(args, torch, np, dg, I, dev):
+    """The quantisation workload: each shape one call on a resident bf16 input; value is
+    algorithmic bytes (2 read + 1 written per element, plus the fp32 scales) per second."""
+    fmt = args.formats.split("x")[0]
+    cases = QUANT_CASES
+    if args.shapes:
+        cases = [cases[int(i)] for i in args.shapes.split(",")]
+    calls = []
+    for i, (kind, rows, K) in enumerate(cases):
+        X = torch.from_numpy(I.normal_matrix(90 + i, 1, rows, K)).to(dev).to(torch.bfloat16)
+        Q = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+        srows = rows if kind == "1x128" else -(-rows // 128)
+        S = torch.empty((srows, K // 128), dtype=torch.float32, device=dev)
+        f = dg.dg_quantize_fp8_1x128 if kind == "1x128" else dg.dg_quantize_fp8_128x128
+        nbytes = rows * K * 3 + S.numel() * 4
+        calls.append(dict(name=f"quant_{kind}_{rows}x{K}", fn=(lambda f=f, X=X, Q=Q, S=S:
+                                                             f(X, fmt, Q, S)),
+                          bytes=nbytes, instance=f"quant_{kind}", X=X, kind=kind))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        for c in calls:
+            c["fn"]()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    with torch.cuda.graph(graph, stream=cap):
+        for c in calls:
+            c["fn"]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    spin = _spin_cycles_for(torch, stream, 40e-6 * len(calls) + 50e-6)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in calls] for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        torch.cuda._sleep(spin)
+        for i, c in enumerate(calls):
+            ev[s_][i][0].record(stream)
+            c["fn"]()
+            ev[s_][i][1].record(stream)
+    torch.cuda.synchronize()
+    per = []
+    for i, c in enumerate(calls):
+        us = 1e3 * float(np.mean([ev[s_][i][0].elapsed_time(ev[s_][i][1])
+                                  for s_ in range(args.steps)]))
+        per.append((c["name"], round(us, 3), round(c["bytes"] / us / 1e3, 1)))
+    total = sum(c["bytes"] for c in calls)
+    dom = max(range(len(calls)), key=lambda i: per[i][1])
+    achieved = calls[dom]["bytes"] / (per[dom][1] * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # a bounded sample: the leading rows of the first shape, about a second of work
+        c = calls[0]
+        x = c["X"][:256].cpu().view(torch.int16).numpy().view(np.uint16)
+        t = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t < max(1.0, min(args.cpu_budget_s, 10.0)):
+            oracle.quantize_1x128(x, fmt)
+            reps += 1
+        dt = time.perf_counter() - t
+        cpu = {"value": round(reps * x.size * 3 / dt / 1e9, 4), "unit": "GB/s",
+               "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"{reps} x 1x128 quantisation of 256x{x.shape[1]} bf16 rows "
+                         f"({dt:.1f} s of oracle time)"}
+    line = {
+        "metric": "FP8 TFLOPS and HBM GB/s (as % of MI355X peak) per M,N,K / group shape",
+        "value": round(total / step_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"bf16->fp8{fmt}", "data": "synthetic (seeded N(0,1) bf16)",
+        "config": {"workload": WORKLOAD_TEXT["quant"], "shapes": len(calls),
+                   "parallelism": "single GPU", "step": "one HIP graph of all shapes"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"{calls[dom]['instance']} on {calls[dom]['name']}",
+                     "launch_us": per[dom][1]},
+        "cpu_baseline": cpu,
+        "per_shape": [list(x) for x in per],
+    }
     print(json.dumps(line), flush=True)
 
 

@@ -160,6 +160,34 @@ dg_status dg_grouped_gemm_fp8_masked_ex(const uint8_t *A, int a_format, const fl
                                         int64_t G, int64_t cap, int64_t N, int64_t K,
                                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------------
+ * fp8 quantisation with block scales: the casting step in front of the GEMM, which the
+ * pages leave to the caller (turtlesai.it summary, technical paragraph), in the two
+ * block shapes of the method's fine-grained scaling (chattools.cn, core design ideas):
+ * one scale per 1x128 block of a row (activations, the sA layout) and one per 128x128
+ * block (weights, the sB layout).
+ *
+ * Per block: amax = max |x| in fp32; scale = amax / FMAX in fp32 (FMAX = 448 for E4M3,
+ * 57344 for E5M2; 1 for an all-zero block); each code is x / scale, an IEEE fp32
+ * division, rounded to the nearest value of `format`, ties to even, saturating at
+ * +-FMAX.  So Q * S reproduces X to within half an fp8 step of each block's scale.
+ *
+ * Inputs: X rows x K (row-major, DEVICE), x_dtype DG_IN_F32 (16-byte aligned) or
+ * DG_IN_BF16 (8-byte aligned); values must be finite (non-finite inputs give
+ * unspecified codes and scales, never a fault).  K > 0, K % 128 == 0 (DG_ERR_SHAPE);
+ * rows >= 0 (0: nothing to do).  Outputs (DEVICE, caller-owned, 4-byte aligned):
+ * Q rows x K codes; S rows x K/128 (1x128) or ceil(rows/128) x K/128 (128x128) fp32.
+ * Errors: DG_ERR_SHAPE, DG_ERR_FORMAT (format or x_dtype), DG_ERR_NULL, DG_ERR_ALIGN,
+ * DG_ERR_DEVICE, DG_ERR_HIP, checked in that order.  Asynchronous on `stream`,
+ * graph-capturable, deterministic. */
+#define DG_IN_F32 0
+#define DG_IN_BF16 1
+
+dg_status dg_quantize_fp8_1x128(const void *X, int x_dtype, uint8_t *Q, float *S,
+                                int64_t rows, int64_t K, int format, void *stream);
+dg_status dg_quantize_fp8_128x128(const void *X, int x_dtype, uint8_t *Q, float *S,
+                                  int64_t rows, int64_t K, int format, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,10 @@ def load_library():
         lib.dg_grouped_gemm_fp8_contiguous_ex.restype = I
         lib.dg_grouped_gemm_fp8_contiguous_ex.argtypes = [P, I, P, P, I, P, P, P, I64, I64, I64,
                                                           I64, P, SZ, P]
+        lib.dg_quantize_fp8_1x128.restype = I
+        lib.dg_quantize_fp8_1x128.argtypes = [P, I, P, P, I64, I64, I, P]
+        lib.dg_quantize_fp8_128x128.restype = I
+        lib.dg_quantize_fp8_128x128.argtypes = [P, I, P, P, I64, I64, I, P]
         lib.dg_grouped_gemm_fp8_masked_ex.restype = I
         lib.dg_grouped_gemm_fp8_masked_ex.argtypes = [P, I, P, P, I, P, P, P, I64, I64, I64,
                                                       I64, P, SZ, P]
@@ -233,6 +237,48 @@ def dg_grouped_gemm_fp8_masked(A, sA, B, sB, masked_m, C=None, *, a_format=None,
     if st != 0:
         raise DGError(st, "dg_grouped_gemm_fp8_masked")
     return C
+
+
+DG_IN_F32, DG_IN_BF16 = 0, 1
+_IN_DTYPES = {torch.float32: DG_IN_F32, torch.bfloat16: DG_IN_BF16}
+_FP8_OF = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+
+
+def _quantize(call, X, fmt, scale_rows, Q, S, stream):
+    if fmt not in _FORMATS:
+        raise ValueError(f"unknown fp8 format {fmt!r}")
+    if X.dtype not in _IN_DTYPES:
+        raise TypeError(f"X must be float32 or bfloat16, got {X.dtype}")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D (rows x K)")
+    rows, K = X.shape
+    dev = X.device
+    if not X.is_contiguous():
+        raise ValueError("X must be contiguous")
+    if Q is None:
+        Q = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+    Qb = Q.view(torch.uint8) if Q.dtype in _FP8_DTYPES else Q
+    _check(Qb, "Q", torch.uint8, (rows, K), dev)
+    if S is None:
+        S = torch.empty((scale_rows, K // 128), dtype=torch.float32, device=dev)
+    _check(S, "S", torch.float32, (scale_rows, K // 128), dev)
+    st = getattr(load_library(), call)(_ptr(X), _IN_DTYPES[X.dtype], _ptr(Qb), _ptr(S), rows,
+                                       K, _FORMATS[fmt], _stream(dev, stream))
+    if st != 0:
+        raise DGError(st, call)
+    return Qb.view(_FP8_OF[fmt]), S
+
+
+def dg_quantize_fp8_1x128(X, fmt="e4m3", Q=None, S=None, *, stream=None):
+    """Per-row 1x128 quantisation of X (rows x K, float32 or bfloat16) to fp8 ('e4m3' or
+    'e5m2').  Returns (Q rows x K as a float8 tensor, S rows x K/128 float32)."""
+    return _quantize("dg_quantize_fp8_1x128", X, fmt, X.shape[0], Q, S, stream)
+
+
+def dg_quantize_fp8_128x128(X, fmt="e4m3", Q=None, S=None, *, stream=None):
+    """128x128-block quantisation of X (rows x K, float32 or bfloat16) to fp8.  Returns
+    (Q rows x K as a float8 tensor, S ceil(rows/128) x K/128 float32)."""
+    return _quantize("dg_quantize_fp8_128x128", X, fmt, -(-X.shape[0] // 128), Q, S, stream)
 
 
 def group_sizes_to_idx(sizes, device=None) -> torch.Tensor:

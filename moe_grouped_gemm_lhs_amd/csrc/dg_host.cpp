@@ -330,4 +330,34 @@ dg_status dg_grouped_gemm_fp8_masked(const uint8_t* A, const float* sA, const ui
                                        cap, N, K, workspace, workspace_bytes, stream);
 }
 
+static dg_status quantize(int block128x128, const void* X, int x_dtype, uint8_t* Q, float* S,
+                          int64_t rows, int64_t K, int format, void* stream) {
+  if (rows < 0 || K <= 0 || K % dg::kBlockK != 0 || rows > INT32_MAX || K > INT32_MAX)
+    return DG_ERR_SHAPE;
+  if (rows * (K / dg::kBlockK) > (int64_t)INT32_MAX * 4) return DG_ERR_SHAPE;   // grid
+  if (!valid_format(format) || (x_dtype != DG_IN_F32 && x_dtype != DG_IN_BF16))
+    return DG_ERR_FORMAT;
+  if (rows == 0) return DG_OK;
+  if (!X || !Q || !S) return DG_ERR_NULL;
+  if (!aligned(X, x_dtype == DG_IN_F32 ? 16 : 8) || !aligned(Q, 4) || !aligned(S, 4))
+    return DG_ERR_ALIGN;
+  int num_cus = 0;
+  const dg_status st = check_device(&num_cus);
+  if (st != DG_OK) return st;
+  (void)hipGetLastError();
+  dg::launch_quantize(block128x128, format, x_dtype == DG_IN_BF16, X, Q, S, rows, K,
+                      (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
+}
+
+dg_status dg_quantize_fp8_1x128(const void* X, int x_dtype, uint8_t* Q, float* S, int64_t rows,
+                                int64_t K, int format, void* stream) {
+  return quantize(0, X, x_dtype, Q, S, rows, K, format, stream);
+}
+
+dg_status dg_quantize_fp8_128x128(const void* X, int x_dtype, uint8_t* Q, float* S,
+                                  int64_t rows, int64_t K, int format, void* stream) {
+  return quantize(1, X, x_dtype, Q, S, rows, K, format, stream);
+}
+
 }  // extern "C"

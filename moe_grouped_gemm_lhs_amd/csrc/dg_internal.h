@@ -63,4 +63,8 @@ struct Instance {
 // Table of all instances compiled into the library (defined in dg_kernels.hip).
 const Instance* instances(int* count);
 
+// fp8 block quantisation launch (defined in dg_quant.hip); arguments already validated.
+void launch_quantize(int block128x128, int fmt, int bf16, const void* X, uint8_t* Q, float* S,
+                     int64_t rows, int64_t K, hipStream_t stream);
+
 }  // namespace dg

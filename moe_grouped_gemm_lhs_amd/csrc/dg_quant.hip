@@ -1,0 +1,175 @@
+// dg_quant.hip -- fp8 quantisation with block scales for gfx950: the casting step in
+// front of the GEMM (turtlesai.it summary, technical paragraph: casting is the user's
+// job; the block shapes are the method's fine-grained scaling).
+//
+// Per block (1x128 along a row, or 128x128): amax = max |x| in fp32; scale = amax /
+// FMAX in fp32 (FMAX = 448 for E4M3, 57344 for E5M2; 1 for an all-zero block); each
+// code is x / scale (an IEEE fp32 division) rounded to the nearest fp8 value, ties to
+// even, saturating at +-FMAX.  Inputs are finite fp32 or bf16.  Memory-bound: every
+// thread moves 16 bytes of fp32 (8 of bf16) per load and writes 4 codes at once; the
+// per-element work is three fp32 operations for the quotient and the hardware's fp8
+// conversion.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+template <int FMT>
+__device__ __forceinline__ float fp8_max() {
+  return FMT == kFmtE5M2 ? 57344.0f : 448.0f;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load4(const void* X, int64_t i, float (&x)[4]) {
+  if (BF16) {
+    const uint2 u = *(const uint2*)((const uint16_t*)X + i);
+    x[0] = __uint_as_float(u.x << 16);
+    x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(u.y << 16);
+    x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  } else {
+    const float4 f = *(const float4*)((const float*)X + i);
+    x[0] = f.x;
+    x[1] = f.y;
+    x[2] = f.z;
+    x[3] = f.w;
+  }
+}
+
+// x / scale rounded to nearest fp32, from a correctly rounded reciprocal r = 1/scale:
+// y = x*r is within an ulp of the quotient and the residual x - y*scale is exact (one
+// fma), so y + r*residual rounded once is the correctly rounded quotient (Markstein's
+// theorem; no overflow or underflow here: |x| <= amax = scale * FMAX).  The sign comes
+// from x (scale > 0), which also keeps the sign of a zero.
+__device__ __forceinline__ float div_by_scale(float x, float scale, float r) {
+  const float y = x * r;
+  const float e = __builtin_fmaf(-y, scale, x);
+  return __builtin_copysignf(__builtin_fmaf(e, r, y), x);
+}
+
+// Four codes: the quotients saturated to +-FMAX, then converted by the hardware's
+// round-to-nearest-even fp8 conversion (OCP E4M3 / E5M2 on gfx950).
+template <int FMT>
+__device__ __forceinline__ uint32_t pack4(const float (&x)[4], float scale, float r) {
+  const float m = fp8_max<FMT>();
+  float q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(div_by_scale(x[i], scale, r), -m), m);
+  int v;
+  if (FMT == kFmtE5M2) {
+    v = __builtin_amdgcn_cvt_pk_bf8_f32(q[0], q[1], 0, false);
+    v = __builtin_amdgcn_cvt_pk_bf8_f32(q[2], q[3], v, true);
+  } else {
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], v, true);
+  }
+  return (uint32_t)v;
+}
+
+// 1x128 blocks: 32 lanes (half a wave) per block, 4 elements each; 8 blocks per
+// 256-thread workgroup.  Block b is row b / nkb, K block b % nkb, and its scale goes
+// to S[b] (S is rows x nkb).
+template <int FMT, bool BF16>
+__global__ void __launch_bounds__(256)
+quant_1x128_kernel(const void* X, uint8_t* Q, float* S, int64_t nblk, int nkb, int64_t K) {
+  const int64_t b = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (b >= nblk) return;                                   // uniform per half wave
+  const int l = threadIdx.x & 31;
+  const int64_t r = b / nkb;
+  const int64_t i = r * K + (b - r * nkb) * kBlockK + l * 4;
+  float x[4];
+  load4<BF16>(X, i, x);
+  float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+  const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<FMT>();
+  const float rcp = 1.0f / scale;                          // correctly rounded
+  *(uint32_t*)(Q + i) = pack4<FMT>(x, scale, rcp);
+  if (l == 0) S[b] = scale;
+}
+
+// 128x128 blocks: one 256-thread workgroup per block; thread t covers columns
+// 4(t % 32) .. +3 of rows t / 32 + 8j, j = 0..15 (rows past the matrix are skipped).
+template <int FMT, bool BF16>
+__global__ void __launch_bounds__(256)
+quant_128x128_kernel(const void* X, uint8_t* Q, float* S, int64_t rows, int nkb, int64_t K) {
+  __shared__ float wave_max[4];
+  const int64_t b = blockIdx.x;
+  const int64_t rb = b / nkb;
+  const int kb = (int)(b - rb * nkb);
+  const int t = threadIdx.x;
+  const int64_t col = (int64_t)kb * kBlockK + (t & 31) * 4;
+  const int64_t row0 = rb * kBlockK + (t >> 5);
+  float x[16][4];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int64_t r = row0 + 8 * j;
+    if (r < rows) {
+      load4<BF16>(X, r * K + col, x[j]);
+    } else {
+      x[j][0] = x[j][1] = x[j][2] = x[j][3] = 0.0f;
+    }
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x[j][0]), fabsf(x[j][1])),
+                             fmaxf(fabsf(x[j][2]), fabsf(x[j][3]))));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((t & 63) == 0) wave_max[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<FMT>();
+  const float rcp = 1.0f / scale;                          // correctly rounded
+  if (t == 0) S[b] = scale;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int64_t r = row0 + 8 * j;
+    if (r < rows) *(uint32_t*)(Q + r * K + col) = pack4<FMT>(x[j], scale, rcp);
+  }
+}
+
+template <int FMT, bool BF16>
+void launch_1x128(const void* X, uint8_t* Q, float* S, int64_t rows, int64_t K,
+                  hipStream_t stream) {
+  const int nkb = (int)(K / kBlockK);
+  const int64_t nblk = rows * nkb;
+  hipLaunchKernelGGL((quant_1x128_kernel<FMT, BF16>), dim3((unsigned)((nblk + 7) / 8)),
+                     dim3(256), 0, stream, X, Q, S, nblk, nkb, K);
+}
+
+template <int FMT, bool BF16>
+void launch_128x128(const void* X, uint8_t* Q, float* S, int64_t rows, int64_t K,
+                    hipStream_t stream) {
+  const int nkb = (int)(K / kBlockK);
+  const int64_t nblk = ((rows + kBlockK - 1) / kBlockK) * nkb;
+  hipLaunchKernelGGL((quant_128x128_kernel<FMT, BF16>), dim3((unsigned)nblk), dim3(256), 0,
+                     stream, X, Q, S, rows, nkb, K);
+}
+
+}  // namespace
+
+// Host-side dispatch over (block shape, format, input type); the caller has validated
+// every argument.
+void launch_quantize(int block128x128, int fmt, int bf16, const void* X, uint8_t* Q, float* S,
+                     int64_t rows, int64_t K, hipStream_t stream) {
+  if (block128x128) {
+    if (fmt == kFmtE5M2)
+      bf16 ? launch_128x128<kFmtE5M2, true>(X, Q, S, rows, K, stream)
+           : launch_128x128<kFmtE5M2, false>(X, Q, S, rows, K, stream);
+    else
+      bf16 ? launch_128x128<kFmtE4M3, true>(X, Q, S, rows, K, stream)
+           : launch_128x128<kFmtE4M3, false>(X, Q, S, rows, K, stream);
+  } else {
+    if (fmt == kFmtE5M2)
+      bf16 ? launch_1x128<kFmtE5M2, true>(X, Q, S, rows, K, stream)
+           : launch_1x128<kFmtE5M2, false>(X, Q, S, rows, K, stream);
+    else
+      bf16 ? launch_1x128<kFmtE4M3, true>(X, Q, S, rows, K, stream)
+           : launch_1x128<kFmtE4M3, false>(X, Q, S, rows, K, stream);
+  }
+}
+
+}  // namespace dg
