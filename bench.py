@@ -150,7 +150,7 @@ def main():
         inst = dg.dg_instance_name(kind_id, p.M if p.kind != "contiguous" else p.rows, p.N, p.K, p.G)
         problems.append(p)
         calls.append(dict(name=I.case_name(case), fn=fn, flops=flops, bytes=nbytes,
-                          instance=inst))
+                          instance=inst, masked_m=mm if p.kind == "masked" else None))
     torch.cuda.synchronize()
     gen_s = time.time() - t0
     print(f"[bench] {len(calls)} shapes resident in HBM ({gen_s:.1f} s to generate)",
@@ -245,6 +245,10 @@ def main():
     roof["kernel"] = f"{d['instance']} on {d['name']}"
     roof["launch_us"] = d["us"]
 
+    graph_latency = None
+    if args.workload == "masked":
+        graph_latency = masked_graph_latency(torch, np, dev, problems, calls, args.steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(problems, calls, args.cpu_budget_s, hbm_bound)
@@ -267,10 +271,47 @@ def main():
         "cpu_baseline": cpu,
         "per_shape": [[q["name"], q["us"], q["tflops"], q["gbs"]] for q in per],
     }
+    if graph_latency is not None:
+        line["masked_decode_latency_us"] = graph_latency
     if args.detail:
         with open(args.detail, "w") as f:
             json.dump(dict(line=line, per_shape=per), f, indent=1)
     print(json.dumps(line), flush=True)
+
+
+def masked_graph_latency(torch, np, dev, problems, calls, steps):
+    """Launch-inclusive latency of one masked call per decode step with fresh counts: each
+    step writes new masked_m values (a small device copy from a table of seeded draws)
+    and then runs the call, either eagerly or by replaying a HIP graph captured once.
+    Per case: [name, eager us/step, graph us/step], wall clock over `steps` steps."""
+    out = []
+    for p, c in zip(problems, calls):
+        mm = c["masked_m"]
+        saved = mm.clone()
+        draws = np.random.default_rng(p.seed + 1000).integers(0, p.M + 1, (16, p.G))
+        table = torch.from_numpy(draws.astype(np.int32)).to(dev)
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.graph(graph, stream=side):
+            c["fn"]()
+        torch.cuda.synchronize()
+        res = [c["name"]]
+        for use_graph in (False, True):
+            for i in range(3):
+                mm.copy_(table[i % 16])
+                graph.replay() if use_graph else c["fn"]()
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for i in range(steps):
+                mm.copy_(table[i % 16])
+                graph.replay() if use_graph else c["fn"]()
+            torch.cuda.synchronize()
+            res.append(round((time.perf_counter() - t) * 1e6 / steps, 2))
+        mm.copy_(saved)
+        out.append(res)
+    torch.cuda.synchronize()
+    return out
 
 
 def bench_quant(args, torch, np, dg, I, dev):
