@@ -188,6 +188,16 @@ dg_status dg_quantize_fp8_1x128(const void *X, int x_dtype, uint8_t *Q, float *S
 dg_status dg_quantize_fp8_128x128(const void *X, int x_dtype, uint8_t *Q, float *S,
                                   int64_t rows, int64_t K, int format, void *stream);
 
+/* Transposition of a byte matrix (fp8 codes): Y (cols x rows) = X (rows x cols)^T, both
+ * row-major DEVICE buffers, 16-byte aligned, rows and cols multiples of 16.  The calls
+ * above take the NT layout only and leave transposition to the caller (turtlesai.it
+ * summary, technical paragraph); this turns a K x N operand into the N x K one they
+ * take.  (Its 128x128 scale matrix transposes as an ordinary small fp32 matrix.)
+ * Errors: DG_ERR_SHAPE, DG_ERR_NULL, DG_ERR_ALIGN, DG_ERR_DEVICE, DG_ERR_HIP, in that
+ * order; rows or cols 0: nothing to do.  Asynchronous on `stream`. */
+dg_status dg_transpose_fp8(const uint8_t *X, uint8_t *Y, int64_t rows, int64_t cols,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

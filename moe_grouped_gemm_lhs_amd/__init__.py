@@ -10,5 +10,5 @@ from .binding import (DG_CONTIGUOUS, DG_DENSE, DG_FP8_E4M3, DG_FP8_E5M2,  # noqa
                       dg_get_m_alignment_for_contiguous_layout,
                       dg_grouped_gemm_fp8_contiguous, dg_grouped_gemm_fp8_masked,
                       dg_instance_name, dg_quantize_fp8_128x128, dg_quantize_fp8_1x128,
-                      dg_status_string, dg_workspace_bytes, group_sizes_to_idx,
+                      dg_status_string, dg_transpose_fp8, dg_workspace_bytes, group_sizes_to_idx,
                       load_library)

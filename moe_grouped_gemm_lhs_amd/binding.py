@@ -69,6 +69,8 @@ def load_library():
         lib.dg_quantize_fp8_1x128.argtypes = [P, I, P, P, I64, I64, I, P]
         lib.dg_quantize_fp8_128x128.restype = I
         lib.dg_quantize_fp8_128x128.argtypes = [P, I, P, P, I64, I64, I, P]
+        lib.dg_transpose_fp8.restype = I
+        lib.dg_transpose_fp8.argtypes = [P, P, I64, I64, P]
         lib.dg_grouped_gemm_fp8_masked_ex.restype = I
         lib.dg_grouped_gemm_fp8_masked_ex.argtypes = [P, I, P, P, I, P, P, P, I64, I64, I64,
                                                       I64, P, SZ, P]
@@ -279,6 +281,27 @@ def dg_quantize_fp8_128x128(X, fmt="e4m3", Q=None, S=None, *, stream=None):
     """128x128-block quantisation of X (rows x K, float32 or bfloat16) to fp8.  Returns
     (Q rows x K as a float8 tensor, S ceil(rows/128) x K/128 float32)."""
     return _quantize("dg_quantize_fp8_128x128", X, fmt, -(-X.shape[0] // 128), Q, S, stream)
+
+
+def dg_transpose_fp8(X, Y=None, *, stream=None):
+    """Y (cols x rows) = X (rows x cols)^T for a byte / fp8 matrix on the GPU (rows and
+    cols multiples of 16).  Y keeps X's dtype."""
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    Xb = X.view(torch.uint8) if X.dtype in _FP8_DTYPES else X
+    if Xb.dtype != torch.uint8:
+        raise TypeError(f"X must be uint8 or float8, got {X.dtype}")
+    rows, cols = Xb.shape
+    dev = Xb.device
+    _check(Xb, "X", torch.uint8, (rows, cols), dev)
+    if Y is None:
+        Y = torch.empty((cols, rows), dtype=X.dtype, device=dev)
+    Yb = Y.view(torch.uint8) if Y.dtype in _FP8_DTYPES else Y
+    _check(Yb, "Y", torch.uint8, (cols, rows), dev)
+    st = load_library().dg_transpose_fp8(_ptr(Xb), _ptr(Yb), rows, cols, _stream(dev, stream))
+    if st != 0:
+        raise DGError(st, "dg_transpose_fp8")
+    return Y
 
 
 def group_sizes_to_idx(sizes, device=None) -> torch.Tensor:

@@ -360,4 +360,19 @@ dg_status dg_quantize_fp8_128x128(const void* X, int x_dtype, uint8_t* Q, float*
   return quantize(1, X, x_dtype, Q, S, rows, K, format, stream);
 }
 
+dg_status dg_transpose_fp8(const uint8_t* X, uint8_t* Y, int64_t rows, int64_t cols,
+                           void* stream) {
+  if (rows < 0 || cols < 0 || rows % 16 != 0 || cols % 16 != 0) return DG_ERR_SHAPE;
+  if (((rows + 63) / 64) * ((cols + 63) / 64) > INT32_MAX) return DG_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return DG_OK;
+  if (!X || !Y) return DG_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(Y, 16)) return DG_ERR_ALIGN;
+  int num_cus = 0;
+  const dg_status st = check_device(&num_cus);
+  if (st != DG_OK) return st;
+  (void)hipGetLastError();
+  dg::launch_transpose_u8(X, Y, rows, cols, (hipStream_t)stream);
+  return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
+}
+
 }  // extern "C"

@@ -173,3 +173,52 @@ void launch_quantize(int block128x128, int fmt, int bf16, const void* X, uint8_t
 }
 
 }  // namespace dg
+
+// ------------------------------------------------------------------------------------
+// Byte-matrix transposition (fp8 codes), for operands stored the other way round: the
+// pages' calls take B as N x K (NT layout only) and leave transposition to the caller
+// (turtlesai.it summary, technical paragraph).  64x64-byte tiles through LDS: each of
+// the 256 threads loads one 16-byte row segment and stores one 16-byte segment of the
+// transposed tile; rows and columns are multiples of 16, so segments never straddle an
+// edge.
+namespace dg {
+namespace {
+
+__global__ void __launch_bounds__(256)
+transpose_u8_kernel(const uint8_t* __restrict__ X, uint8_t* __restrict__ Y, int64_t rows,
+                    int64_t cols, int64_t tiles_c) {
+  __shared__ uint8_t tile[64][64 + 4];
+  const int64_t tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
+  const int t = threadIdx.x;
+  const int seg = t & 3, line = t >> 2;                 // 4 segments of 16 bytes per line
+  {
+    const int64_t r = tr * 64 + line, c = tc * 64 + seg * 16;
+    if (r < rows && c < cols) {
+      const uint4 v = *(const uint4*)(X + r * cols + c);
+      *(uint4*)&tile[line][seg * 16] = v;
+    }
+  }
+  __syncthreads();
+  // output line = input column tc*64 + line, its 16 bytes = input rows tr*64 + 16*seg ..
+  const int64_t orow = tc * 64 + line, ocol = tr * 64 + seg * 16;
+  if (orow < cols && ocol < rows) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = (uint32_t)tile[seg * 16 + 4 * i][line] | ((uint32_t)tile[seg * 16 + 4 * i + 1][line] << 8) |
+             ((uint32_t)tile[seg * 16 + 4 * i + 2][line] << 16) |
+             ((uint32_t)tile[seg * 16 + 4 * i + 3][line] << 24);
+    *(uint4*)(Y + orow * rows + ocol) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+}  // namespace
+
+void launch_transpose_u8(const uint8_t* X, uint8_t* Y, int64_t rows, int64_t cols,
+                         hipStream_t stream) {
+  const int64_t tiles_r = (rows + 63) / 64, tiles_c = (cols + 63) / 64;
+  hipLaunchKernelGGL(transpose_u8_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0,
+                     stream, X, Y, rows, cols, tiles_c);
+}
+
+}  // namespace dg

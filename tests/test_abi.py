@@ -102,6 +102,18 @@ def test_quantize_validation_codes(lib):
         assert f(A16, 0, A16, A4 + 1, 64, 128, 0, None) == 3
 
 
+def test_transpose_validation_codes(lib):
+    f = lib.dg_transpose_fp8
+    assert f(A16, A16, 64, 100, None) == 2
+    assert f(A16, A16, 8, 64, None) == 2
+    assert f(A16, A16, -16, 64, None) == 2
+    assert f(None, A16, 0, 64, None) == 0
+    assert f(None, A16, 64, 64, None) == 1
+    assert f(A16, None, 64, 64, None) == 1
+    assert f(A16 + 4, A16, 64, 64, None) == 3
+    assert f(A16, A16 + 8, 64, 64, None) == 3
+
+
 def test_grouped_validation_codes(lib):
     c = lib.dg_grouped_gemm_fp8_contiguous
     assert c(A16, A4, A16, A4, A4, A16, 256, 128, 128, 0, None, 0, None) == 2   # G < 1

@@ -1,7 +1,8 @@
 """GPU parity of the fp8 block quantisers (dg_quantize_fp8_1x128 / _128x128) against the
 CPU oracle: codes and scales must match bit for bit (fp32 and bf16 inputs, E4M3 and
 E5M2, ragged row counts, exact rounding ties, all-zero blocks, saturation), and
-quantise-then-GEMM on the GPU must agree with the oracle doing both steps."""
+quantise-then-GEMM on the GPU must agree with the oracle doing both steps.  Also the
+byte transposition (dg_transpose_fp8) against NumPy's transpose, bit for bit."""
 import numpy as np
 import pytest
 
@@ -101,3 +102,30 @@ def test_quantize_then_gemm(fmt):
     c_ref = oracle.gemm_fp8_nt(qa, sa, qb, sb, a_fmt=fmt, b_fmt=fmt)
     c_gpu = C.view(torch.int16).cpu().numpy().view(np.uint16)
     assert_within_tolerance(c_gpu, c_ref, np.ones((M, N), bool), f"quantise+gemm {fmt}")
+
+
+@pytest.mark.parametrize("rows,cols", [(16, 16), (64, 64), (112, 2112), (2048, 7168),
+                                       (48, 80)])
+def test_transpose_bit_exact(rows, cols):
+    rng = np.random.default_rng(rows + cols)
+    x = rng.integers(0, 256, (rows, cols), dtype=np.uint8)
+    gu.say(f"[case] transpose {rows}x{cols}")
+    Y = dg.dg_transpose_fp8(torch.from_numpy(x).to(gu.DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(Y.cpu().numpy(), x.T)
+
+
+def test_transpose_then_gemm():
+    """B stored K x N (the layout the NT calls do not take), transposed on the GPU, then
+    the GEMM: equal to the oracle on the N x K operand."""
+    M, N, K = 130, 2112, 512
+    p = I.make_dense(M, N, K, seed=85)
+    Bkn = torch.from_numpy(np.ascontiguousarray(p.B.T)).to(gu.DEV)        # K x N
+    B = dg.dg_transpose_fp8(Bkn)
+    A, sA, _, sB = gu.device_operands(p)
+    C = dg.dg_gemm_fp8_nt(A, sA, B, sB)
+    torch.cuda.synchronize()
+    c_gpu = C.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(B.cpu().numpy(), p.B)
+    assert_within_tolerance(c_gpu, oracle.gemm_fp8_nt(p.A, p.sA, p.B, p.sB),
+                            np.ones((M, N), bool), "transpose+gemm")
