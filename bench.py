@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches, not a graph")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--detail", default="", help="write per-shape details to this JSON file")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain device-to-device copy of MIB MiB (a kernel of "
+                         "known traffic, to scale HBM byte counters under a profiler)")
     return ap.parse_args()
 
 
@@ -98,6 +101,15 @@ def main():
     torch.cuda.set_device(dev)
     dg.load_library()
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        del src, dst
     if args.workload == "quant":
         return bench_quant(args, torch, np, dg, I, dev)
     cases = workload_cases(args.workload)
@@ -244,6 +256,7 @@ def main():
                     unit="TFLOP/s", frac=round(achieved / FP8_PEAK_TFLOPS, 4), traffic=None)
     roof["kernel"] = f"{d['instance']} on {d['name']}"
     roof["launch_us"] = d["us"]
+    roof["traffic"] = _profiled_traffic(d["instance"], d["name"])
 
     graph_latency = None
     if args.workload == "masked":
@@ -399,6 +412,39 @@ def bench_quant(args, torch, np, dg, I, dev):
         "per_shape": [list(x) for x in per],
     }
     print(json.dumps(line), flush=True)
+
+
+_ROOT = os.path.dirname(os.path.abspath(__file__))
+_KERNEL_SOURCES = ["moe_grouped_gemm_lhs_amd/csrc/dg_kernels.hip",
+                   "moe_grouped_gemm_lhs_amd/csrc/dg_internal.h",
+                   "moe_grouped_gemm_lhs_amd/csrc/dg_host.cpp"]
+_TRAFFIC_FILES = {("dense_128x128_stream", "dense_128x7168x16384"):
+                  "profiles/decode_stream_kernel_hbm_traffic.txt"}
+
+
+def _profiled_traffic(instance, shape):
+    """HBM bytes per launch of this kernel on this shape from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or None
+    when there is none or the kernel sources changed since it was taken."""
+    import hashlib
+    rel = _TRAFFIC_FILES.get((instance, shape))
+    if rel is None or not os.path.exists(os.path.join(_ROOT, rel)):
+        return None
+    fields = {}
+    for line in open(os.path.join(_ROOT, rel)):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for src in _KERNEL_SOURCES:
+        with open(os.path.join(_ROOT, src), "rb") as f:
+            h.update(f.read())
+    if fields.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _spin_cycles_for(torch, stream, seconds):
