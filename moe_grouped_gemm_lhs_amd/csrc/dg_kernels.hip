@@ -114,6 +114,10 @@ __device__ __forceinline__ v4i encode_partial(v4f v) {
 }
 __device__ __forceinline__ v4f decode_partial(v4i u) { return __builtin_bit_cast(v4f, ~u); }
 
+// Cache policy of the polling loads: sc1 (device coherent) plus the intrinsic's volatile
+// bit, so that the compiler keeps every poll inside its loop.
+constexpr int kPollAux = (int)0x80000010u;
+
 __device__ __forceinline__ v8i read_frag(const uint8_t* base, int row, int q) {
   const uint8_t* r = base + row * kBlockK;
   const v4i lo = *(const v4i*)(r + ((q ^ (row & 7)) << 4));
@@ -503,11 +507,13 @@ gemm_fp8_kernel(GemmArgs p) {
 // reduced deterministically and in parallel, with no atomics: each contributor writes its
 // fp32 partial in fragment order (one contiguous 1 KB block per 16x16 sub-tile) with
 // device-coherent (sc1) stores, every value stored bit-inverted so that a zero word
-// means "not written yet" (the workspace starts zero filled).  After its loop, each
-// contributor reduces every n-th fragment of the tile (its own share): it polls each
-// contributor's slot until all of its words are non-zero, sums the contributors in
-// workgroup order, stores those fragments as bf16 and writes zeros back, which leaves
-// the workspace zero filled for the next call.  Every workgroup writes all its partials
+// means "not written yet" (the workspace starts zero filled).  The tile's reducers are
+// the contributors whose range ends inside it (all but the last contributor, unless that
+// one's range ends with the tile); after its loop, each reducer takes every nr-th
+// fragment of the tile (nr reducers): it polls each contributor's slot until all of its
+// words are non-zero, sums the contributors in workgroup order, stores those fragments
+// as bf16 and writes zeros back, which leaves the workspace zero filled for the next
+// call.  Every workgroup writes all its partials
 // before it waits on any, and the persistent grid never exceeds the CU count with one
 // workgroup per CU (the LDS budget admits no second), so all contributors are resident
 // and every wait ends; the wait is bounded all the same.  A workgroup holds at most two
@@ -622,28 +628,32 @@ gemm_fp8_stream_kernel(GemmArgs p) {
     in_tile = 0;
   }
 
-  // ---- reduction of the shared tiles: this workgroup's share of each.  Wave w takes
-  // the share's fragments w, w + W, ... two at a time; for each pair it fetches the
-  // contributors' 1 KB slots CB at a time with all loads in flight together (polled
-  // until written), sums them in workgroup order, zeroes the slots, and stores bf16.
-  // Waves work independently: no barrier.
+  // ---- reduction of a shared tile.  It is split among its reducers: the contributors
+  // whose range ends inside it, i.e. all but the last one, unless that one's range ends
+  // with the tile too.  The last contributor stored its partial when it moved on to the
+  // next tile, so the reducers only wait for one another, and a workgroup reduces at most
+  // one tile: the last of its range.  Reducer r of nr takes fragments r, r + nr, ...;
+  // wave w takes the share's fragments w, w + W, ... two at a time; for each pair it
+  // fetches the contributors' 1 KB slots CB at a time with all loads in flight together
+  // (polled until written), sums them in workgroup order, zeroes the slots, and stores
+  // bf16.  Waves work independently: no barrier.
   constexpr int F = C::W * TI * TJ;                        // fragments per tile
   constexpr int CB = 8;                                    // contributors per fetch
   constexpr int kPastBuffer = 0x7FFFFF00;                  // beyond part_rsrc's range
-#pragma unroll 1
-  for (int seg = 0; seg < 2; ++seg) {
-    const int t = shared_tile[seg];
-    if (t < 0) continue;
+  const int t_last = (int)((i_end - 1) / nkb);
+  const int t = shared_tile[1] >= 0 ? shared_tile[1] : (shared_tile[0] == t_last ? t_last : -1);
+  if (t >= 0) {
     const long x0 = (long)t * nkb, x1 = x0 + nkb - 1;
     const long g_first = ((x0 + 1) * G + W - 1) / W - 1;
     const long g_last = ((x1 + 1) * G + W - 1) / W - 1;
     const int n = (int)(g_last - g_first + 1);
-    const int me = (int)(g - g_first);
-    const int fm = me < F ? (F - me + n - 1) / n : 0;     // fragments me, me+n, ...
+    const int nr = n - 1 + (stream_start<C>(g_last + 1, W, G) == x1 + 1 ? 1 : 0);
+    const int me = (int)(g - g_first);                     // this workgroup's reducer index
+    const int fm = me < F ? (F - me + nr - 1) / nr : 0;   // fragments me, me+nr, ...
 #pragma unroll 1
     for (int k = wave; k < fm; k += 2 * C::W) {
       const bool two = k + C::W < fm;
-      const int f0 = me + n * k, f1 = me + n * (k + C::W);
+      const int f0 = me + nr * k, f1 = me + nr * (k + C::W);
       v4f sum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 1
       for (int c0 = 0; c0 < n; c0 += CB) {
@@ -670,7 +680,7 @@ gemm_fp8_stream_kernel(GemmArgs p) {
 #pragma unroll
             for (int u = 0; u < CB; ++u)
               raw[r][u] = __builtin_amdgcn_raw_buffer_load_b128(part_rsrc, off[r][u], 0,
-                                                                16 /* sc1 */);
+                                                                kPollAux);
           bool mine = true;
 #pragma unroll
           for (int r = 0; r < 2; ++r)
