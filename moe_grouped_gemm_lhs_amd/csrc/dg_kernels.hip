@@ -75,12 +75,13 @@ __device__ __forceinline__ void wait_stages_ahead(int ahead) {
 }
 
 // The same for a kernel instance's copies: PER_STAGE per stage for the waves that also
-// copy scales, PER_N for the others (`wave` is uniform).
+// copy scales, PER_N for the other copy waves; waves that copy nothing do not wait (the
+// barrier that follows orders them after the copy waves' waits).  `wave` is uniform.
 template <class C, int A>
 __device__ __forceinline__ void wait_stage_copies(int wave, int ahead) {
   if (wave < C::S_WAVES)
     wait_stages_ahead<C::PER_STAGE, A>(ahead);
-  else
+  else if (wave < C::CW)
     wait_stages_ahead<C::PER_N, A>(ahead);
 }
 
@@ -139,40 +140,47 @@ __device__ __forceinline__ void stage_barrier() {
 // Compile-time shape of one kernel instance.
 // B_NT: B blocks are read by exactly one workgroup (decode shapes), so they are loaded
 // non-temporal.  FMT_A / FMT_B: operand formats (0: E4M3, 1: E5M2).
+// CW_: how many waves issue the stage copies (0: all).  A wave's copies queue in the CU's
+// address unit behind the other waves' (one 1 KB copy per 16 clocks at most), and a wave
+// cannot start its MFMAs until its own copies are issued; with two waves per SIMD, giving
+// all copies to the first wave of each SIMD lets the second start computing at once.
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, bool B_NT_ = false,
-          int FMT_A_ = 0, int FMT_B_ = 0>
+          int FMT_A_ = 0, int FMT_B_ = 0, int CW_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int STAGES = STAGES_;
   static constexpr bool B_NT = B_NT_;
   static constexpr int FMT_A = FMT_A_, FMT_B = FMT_B_;
   static constexpr int W = WAVES_M * WAVES_N;
+  static constexpr int CW = CW_ ? CW_ : W;      // copy waves: 0 .. CW-1
   static constexpr int NT = 64 * W;
   static constexpr int WM = BM / WAVES_M;       // rows per wave
   static constexpr int WN = BN / WAVES_N;       // columns per wave
   static constexpr int TI = WM / 16;            // 16-row sub-tiles per wave
   static constexpr int TJ = WN / 16;            // 16-column sub-tiles per wave
-  // 1 KB direct loads (8 rows) per wave per stage; when the 8-row blocks do not split
-  // evenly over the waves, the last loads fill padding rows that are never read
-  static constexpr int A_DMA = (BM / 8 + W - 1) / W;
-  static constexpr int B_DMA = (BN / 8 + W - 1) / W;
-  static constexpr int A_BYTES = A_DMA * W * 8 * kBlockK;
-  static constexpr int B_BYTES = B_DMA * W * 8 * kBlockK;
+  // 1 KB direct loads (8 rows) per copy wave per stage; when the 8-row blocks do not
+  // split evenly over the copy waves, the last loads fill padding rows that are never read
+  static constexpr int A_DMA = (BM / 8 + CW - 1) / CW;
+  static constexpr int B_DMA = (BN / 8 + CW - 1) / CW;
+  static constexpr int A_BYTES = A_DMA * CW * 8 * kBlockK;
+  static constexpr int B_BYTES = B_DMA * CW * 8 * kBlockK;
   static constexpr int NBV = (BN + 127) / 128 + 1;   // sB blocks a tile can touch
-  // scale slots: sA for BM rows, then the tile's sB values; only the first S_WAVES
-  // waves copy them (one 4-byte-per-lane copy each per stage)
-  static constexpr int S_WAVES = (BM + NBV + 63) / 64;
-  static constexpr int S_FLOATS = 64 * S_WAVES;
+  // scale slots: sA for BM rows, then the tile's sB values, 64 per 4-byte-per-lane copy;
+  // the first S_WAVES waves issue S_PER such copies each per stage
+  static constexpr int S_COPIES = (BM + NBV + 63) / 64;
+  static constexpr int S_WAVES = S_COPIES < CW ? S_COPIES : CW;
+  static constexpr int S_PER = (S_COPIES + CW - 1) / CW;
+  static constexpr int S_FLOATS = 64 * S_PER * S_WAVES;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + 4 * S_FLOATS;
-  // copies per stage of a wave without / with a scale copy
+  // copies per stage of a copy wave without / with scale copies
   static constexpr int PER_N = A_DMA + B_DMA;
-  static constexpr int PER_STAGE = PER_N + 1;
+  static constexpr int PER_STAGE = PER_N + S_PER;
   // every wave's columns fall inside one 128-column scale block
   static constexpr bool ONE_NB =
       (128 % WN == 0) && ((BN % 128 == 0) || (128 % BN == 0));
   static_assert(BM % (16 * WAVES_M) == 0 && BN % (16 * WAVES_N) == 0, "tile shape");
   static_assert(BM % 8 == 0 && BN % 8 == 0, "direct-load blocks");
-  static_assert(BM + NBV <= S_FLOATS && S_WAVES <= W, "scale slots");
+  static_assert(BM + NBV <= S_FLOATS && S_WAVES <= CW && CW <= W, "scale slots");
   static_assert(PER_N >= 1, "every wave copies operand bytes");
   static_assert(STAGES >= 2 && (STAGES - 2) * PER_STAGE < 64, "pipeline depth");
   static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
@@ -258,6 +266,7 @@ struct TileCtx {
 // Direct-to-LDS copy of K block kb of the tile into stage `st`.
 template <class C>
 __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const TileCtx& c, int kb) {
+  if (c.wave >= C::CW) return;             // not a copy wave
   const int sub = c.lane >> 3;             // row inside the 8-row block
   const int ch = (c.lane & 7) ^ sub;       // global chunk for this lane's slot
 #pragma unroll
@@ -274,15 +283,19 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
                            st + C::A_BYTES + cb * 1024);
   }
   if (c.wave < C::S_WAVES) {
-    const int s = c.wave * 64 + c.lane;
-    const float* src;
-    if (s < C::BM)
-      src = c.sA + (size_t)(c.a_row0 + min(s, c.rows - 1)) * c.nkb + kb;
-    else if (s < C::BM + C::NBV)
-      src = c.sBg + (size_t)min(c.nb_first + s - C::BM, c.nnb - 1) * c.nkb + kb;
-    else
-      src = c.sA + (size_t)c.a_row0 * c.nkb + kb;
-    dma4(src, st + C::A_BYTES + C::B_BYTES + c.wave * 256);
+#pragma unroll
+    for (int it = 0; it < C::S_PER; ++it) {
+      const int slot = c.wave * C::S_PER + it;
+      const int s = slot * 64 + c.lane;
+      const float* src;
+      if (s < C::BM)
+        src = c.sA + (size_t)(c.a_row0 + min(s, c.rows - 1)) * c.nkb + kb;
+      else if (s < C::BM + C::NBV)
+        src = c.sBg + (size_t)min(c.nb_first + s - C::BM, c.nnb - 1) * c.nkb + kb;
+      else
+        src = c.sA + (size_t)c.a_row0 * c.nkb + kb;
+      dma4(src, st + C::A_BYTES + C::B_BYTES + slot * 256);
+    }
   }
 }
 
@@ -756,8 +769,12 @@ int grid_persistent(const GemmArgs& a, int num_cus) {
 }
 
 // Tile shapes, each built for the four operand-format pairs (FA, FB).
-template <int FA, int FB> using Big = Cfg<256, 256, 4, 2, 2, false, FA, FB>;     // 8 waves, 64x128 each
-template <int FA, int FB> using Big224 = Cfg<256, 224, 4, 2, 2, false, FA, FB>;  // non-power-of-two N tile
+template <int FA, int FB> using Big = Cfg<256, 256, 4, 2, 2, false, FA, FB, 4>;     // 8 waves, 64x128 each
+template <int FA, int FB> using Big224 = Cfg<256, 224, 4, 2, 2, false, FA, FB, 4>;  // non-power-of-two N tile
+// the contiguous form's larger per-tile state leaves no registers for the copy waves'
+// doubled address set: all waves copy
+template <int FA, int FB> using BigC = Cfg<256, 256, 4, 2, 2, false, FA, FB>;
+template <int FA, int FB> using Big224C = Cfg<256, 224, 4, 2, 2, false, FA, FB>;
 template <int FA, int FB> using Mid = Cfg<128, 128, 2, 2, 3, false, FA, FB>;     // 4 waves, 64x64 each
 template <int FA, int FB> using Small = Cfg<64, 128, 1, 4, 4, false, FA, FB>;    // 4 waves, 64x32 each
 // stream-K decode instances: 8 waves (a wave's direct-to-LDS copies are issue-bound, so
@@ -791,8 +808,8 @@ static const Instance kInstances[] = {
     DG_STREAM("dense_64x64_stream", Str64n64),
     DG_STREAM("dense_128x128_stream", Str128),
     DG_STREAM("dense_128x64_stream", Str128n64),
-    DG_INST("contig_256x256", kContiguous, Big),
-    DG_INST("contig_256x224", kContiguous, Big224),
+    DG_INST("contig_256x256", kContiguous, BigC),
+    DG_INST("contig_256x224", kContiguous, Big224C),
     DG_INST("contig_128x128", kContiguous, Mid),
     DG_INST("masked_256x256", kMasked, Big),
     DG_INST("masked_128x128", kMasked, Mid),
