@@ -5,7 +5,7 @@
 // For each output tile and each 128-deep K block kb:
 //   1. the e4m3 bytes of A[m0:m0+BM, kb] and B_g[n0:n0+BN, kb], the scales
 //      sA[m0:m0+BM, kb] and the few sB_g[nb, kb] the tile needs are copied global -> LDS
-//      with the direct-to-LDS loads (global_load_lds_dwordx4 / _dword), STAGES blocks
+//      with direct-to-LDS buffer loads (buffer_load_dwordx4 / _dword ... lds), STAGES blocks
 //      ahead, so that HBM/L2 traffic for later blocks overlaps the math of this one;
 //   2. each 16x16 sub-tile's fp32 block partial comes from one
 //      v_mfma_f32_16x16x128_f8f6f4 started from zero;
@@ -85,14 +85,21 @@ __device__ __forceinline__ void wait_stage_copies(int wave, int ahead) {
     wait_stages_ahead<C::PER_N, A>(ahead);
 }
 
-// 16 bytes per lane; AUX is the cache policy (0: default, 2: non-temporal, for operands
-// that are read once and would only evict reused data from the caches).
-template <int AUX = 0>
-__device__ __forceinline__ void dma16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, AUX);
+// Buffer resource over `bytes` bytes from `base` (raw, stride 0): a load at an offset
+// past the end returns zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 4, 0, 0);
+
+// Direct-to-LDS buffer loads: 16 (or 4) bytes per lane at byte offset `off`, the wave's
+// 64 lanes landing contiguously at `lds`.  AUX is the cache policy (0: default,
+// 2: non-temporal, for operands that are read once and would only evict reused data).
+template <int AUX = 0>
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, int off, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, AUX);
+}
+__device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t r, int off, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
@@ -263,38 +270,49 @@ struct TileCtx {
   int wave, lane, wm, wn, q, l16;
 };
 
-// Direct-to-LDS copy of K block kb of the tile into stage `st`.
+// Direct-to-LDS copy of K block kb of the tile into stage `st`.  The copies go through
+// buffer resources that span only the tile's valid rows of A and columns of B (and their
+// scales): a lane whose offset falls past the end reads zeros without touching memory,
+// so the rows and columns past the matrix edge need no clamping and their (never
+// stored) outputs come from zeros.  Every offset is a per-lane VGPR term plus a uniform
+// term, all in the range-checked vector offset.
 template <class C>
 __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const TileCtx& c, int kb) {
   if (c.wave >= C::CW) return;             // not a copy wave
   const int sub = c.lane >> 3;             // row inside the 8-row block
   const int ch = (c.lane & 7) ^ sub;       // global chunk for this lane's slot
+  const int K = c.K;
+  const __amdgpu_buffer_rsrc_t ra = buffer_over(c.A + (size_t)c.a_row0 * K, c.rows * K);
+  const __amdgpu_buffer_rsrc_t rb =
+      buffer_over(c.Bg + (size_t)c.n0 * K, min(C::BN, c.N - c.n0) * K);
+  const int lane_off = sub * K + ch * 16;
 #pragma unroll
   for (int it = 0; it < C::A_DMA; ++it) {
     const int cb = c.wave * C::A_DMA + it;
-    const int row = min(cb * 8 + sub, c.rows - 1);
-    dma16(c.A + (size_t)(c.a_row0 + row) * c.K + kb * kBlockK + ch * 16, st + cb * 1024);
+    copy16<0>(ra, lane_off + (cb * 8 * K + kb * kBlockK), st + cb * 1024);
   }
 #pragma unroll
   for (int it = 0; it < C::B_DMA; ++it) {
     const int cb = c.wave * C::B_DMA + it;
-    const int n = min(c.n0 + cb * 8 + sub, c.N - 1);
-    dma16<C::B_NT ? 2 : 0>(c.Bg + (size_t)n * c.K + kb * kBlockK + ch * 16,
-                           st + C::A_BYTES + cb * 1024);
+    copy16<C::B_NT ? 2 : 0>(rb, lane_off + (cb * 8 * K + kb * kBlockK),
+                            st + C::A_BYTES + cb * 1024);
   }
   if (c.wave < C::S_WAVES) {
+    // slot s < BM: sA of row s; slot BM + j: sB of column block nb_first + j (the slots
+    // after the tile's NBV blocks, and any padding slots, are filled but never read)
+    const __amdgpu_buffer_rsrc_t rsa =
+        buffer_over(c.sA + (size_t)c.a_row0 * c.nkb, c.rows * c.nkb * 4);
+    const __amdgpu_buffer_rsrc_t rsb =
+        buffer_over(c.sBg + (size_t)c.nb_first * c.nkb, (c.nnb - c.nb_first) * c.nkb * 4);
+    const int s_off = c.lane * c.nkb * 4 + kb * 4;
 #pragma unroll
     for (int it = 0; it < C::S_PER; ++it) {
       const int slot = c.wave * C::S_PER + it;
-      const int s = slot * 64 + c.lane;
-      const float* src;
-      if (s < C::BM)
-        src = c.sA + (size_t)(c.a_row0 + min(s, c.rows - 1)) * c.nkb + kb;
-      else if (s < C::BM + C::NBV)
-        src = c.sBg + (size_t)min(c.nb_first + s - C::BM, c.nnb - 1) * c.nkb + kb;
+      uint8_t* dst = st + C::A_BYTES + C::B_BYTES + slot * 256;
+      if (slot * 64 < C::BM)
+        copy4(rsa, s_off + slot * 64 * c.nkb * 4, dst);
       else
-        src = c.sA + (size_t)c.a_row0 * c.nkb + kb;
-      dma4(src, st + C::A_BYTES + C::B_BYTES + slot * 256);
+        copy4(rsb, s_off + (slot * 64 - C::BM) * c.nkb * 4, dst);
     }
   }
 }
@@ -771,9 +789,9 @@ int grid_persistent(const GemmArgs& a, int num_cus) {
 // Tile shapes, each built for the four operand-format pairs (FA, FB).
 template <int FA, int FB> using Big = Cfg<256, 256, 4, 2, 2, false, FA, FB, 4>;     // 8 waves, 64x128 each
 template <int FA, int FB> using Big224 = Cfg<256, 224, 4, 2, 2, false, FA, FB, 4>;  // non-power-of-two N tile
-// the contiguous form's larger per-tile state leaves no registers for the copy waves'
-// doubled address set: all waves copy
-template <int FA, int FB> using BigC = Cfg<256, 256, 4, 2, 2, false, FA, FB>;
+// the contiguous form keeps more per-tile state: its 256x224 tile has no registers to
+// spare for the copy waves' doubled copy set, so all of its waves copy
+template <int FA, int FB> using BigC = Cfg<256, 256, 4, 2, 2, false, FA, FB, 4>;
 template <int FA, int FB> using Big224C = Cfg<256, 224, 4, 2, 2, false, FA, FB>;
 template <int FA, int FB> using Mid = Cfg<128, 128, 2, 2, 3, false, FA, FB>;     // 4 waves, 64x64 each
 template <int FA, int FB> using Small = Cfg<64, 128, 1, 4, 4, false, FA, FB>;    // 4 waves, 64x32 each
