@@ -360,6 +360,9 @@ __device__ __forceinline__ void compute_stage(const uint8_t* __restrict__ st, co
       if (i == 0 && j + 1 < TJ) bf[(j + 1) & 1] = read_frag(Bs, c.wn * WN + 16 * (j + 1) + l16, q);
       part[t] = mfma_fp8_16x16x128<C::FMT_B, C::FMT_A>(bf[j & 1], af[i]);   // B first
     }
+    // keep the promotion behind this step's MFMA: moved ahead of it, it would read a
+    // partial whose MFMA was issued just one MFMA earlier and stall for its latency
+    __builtin_amdgcn_sched_barrier(0);
     if (t >= 2) {
       const int u = t - 2;
       const int j = u / TI, i = u % TI;
