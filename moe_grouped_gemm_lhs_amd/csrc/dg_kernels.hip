@@ -126,11 +126,14 @@ __device__ __forceinline__ v4f decode_partial(v4i u) { return __builtin_bit_cast
 // bit, so that the compiler keeps every poll inside its loop.
 constexpr int kPollAux = (int)0x80000010u;
 
-__device__ __forceinline__ v8i read_frag(const uint8_t* base, int row, int q) {
-  const uint8_t* r = base + row * kBlockK;
-  const v4i lo = *(const v4i*)(r + ((q ^ (row & 7)) << 4));
-  const v4i hi = *(const v4i*)(r + (((q + 4) ^ (row & 7)) << 4));
-  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+// One MFMA operand fragment from LDS (32 bytes per lane: chunks q and q+4 of the lane's
+// row, at their swizzled slots), given the lane's pointers to those two chunks in the
+// operand's first 16-row block: rows r and r + 16k share r & 7 and so the same slots,
+// hence block b sits at a constant offset (an LDS-read immediate).
+__device__ __forceinline__ v8i read_frag_block(const uint8_t* lo, const uint8_t* hi, int b) {
+  const v4i l = *(const v4i*)(lo + b * 16 * kBlockK);
+  const v4i h = *(const v4i*)(hi + b * 16 * kBlockK);
+  return (v8i){l.x, l.y, l.z, l.w, h.x, h.y, h.z, h.w};
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): that fence waits for
@@ -327,13 +330,20 @@ __device__ __forceinline__ void compute_stage(const uint8_t* __restrict__ st, co
   const float* Ss = (const float*)(st + C::A_BYTES + C::B_BYTES);
   const int q = c.q, l16 = c.l16;
 
+  // lane pointers to chunks q and q+4 of this lane's row in the wave's first 16-row
+  // block of A and of B
+  const int lo = l16 * kBlockK + ((q ^ (l16 & 7)) << 4);
+  const int hi = l16 * kBlockK + (((q + 4) ^ (l16 & 7)) << 4);
+  const uint8_t* a_lo = As + c.wm * WM * kBlockK + lo;
+  const uint8_t* a_hi = As + c.wm * WM * kBlockK + hi;
+  const uint8_t* b_lo = Bs + c.wn * WN * kBlockK + lo;
+  const uint8_t* b_hi = Bs + c.wn * WN * kBlockK + hi;
   v8i af[TI];
   float sa[TI];
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
-    const int r = c.wm * WM + 16 * i + l16;
-    af[i] = read_frag(As, r, q);
-    sa[i] = Ss[r];
+    af[i] = read_frag_block(a_lo, a_hi, i);
+    sa[i] = Ss[c.wm * WM + 16 * i + l16];
   }
   float sb[TJ];
 #pragma unroll
@@ -347,7 +357,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* __restrict__ st, co
     for (int i = 0; i < TI; ++i) s_i[i] = sa[i] * sb[0];
   }
   v8i bf[2];
-  bf[0] = read_frag(Bs, c.wn * WN + l16, q);
+  bf[0] = read_frag_block(b_lo, b_hi, 0);
   __builtin_amdgcn_sched_barrier(0);
 
   // software pipeline: MFMA for step t, promotion of step t-2
@@ -357,7 +367,7 @@ __device__ __forceinline__ void compute_stage(const uint8_t* __restrict__ st, co
   for (int t = 0; t < T + 2; ++t) {
     if (t < T) {
       const int j = t / TI, i = t % TI;
-      if (i == 0 && j + 1 < TJ) bf[(j + 1) & 1] = read_frag(Bs, c.wn * WN + 16 * (j + 1) + l16, q);
+      if (i == 0 && j + 1 < TJ) bf[(j + 1) & 1] = read_frag_block(b_lo, b_hi, j + 1);
       part[t] = mfma_fp8_16x16x128<C::FMT_B, C::FMT_A>(bf[j & 1], af[i]);   // B first
     }
     // keep the promotion behind this step's MFMA: moved ahead of it, it would read a
