@@ -164,3 +164,18 @@ def test_instance_selection_is_host_logic(lib):
         ws = b.dg_workspace_bytes(kind, rows, n, k, g)
         assert ws >= 0
     assert b.dg_workspace_bytes(0, 64, 2112, 100, 1) == 0
+
+
+def test_tiled_selection_uses_measured_tile_efficiency(lib):
+    """The tile-shape heuristic (full rounds of tiles over 256 CUs, divided by each shape's
+    measured per-area efficiency) on the bench's prefill and contiguous shapes: 256x224
+    only where it saves a whole round of tiles, never for the contiguous form."""
+    from moe_grouped_gemm_lhs_amd import binding as b
+    dense = {(2112, 7168): "dense_256x224", (24576, 1536): "dense_256x256",
+             (32768, 512): "dense_256x256", (7168, 16384): "dense_256x224",
+             (4096, 7168): "dense_256x256", (7168, 2048): "dense_256x224"}
+    for (n, k), name in dense.items():
+        assert b.dg_instance_name(0, 4096, n, k, 1) == name, (n, k)
+    for rows, n, k, g in [(32768, 4096, 7168, 4), (30592, 4096, 7168, 8),
+                          (32768, 7168, 2048, 8), (24448, 7168, 2048, 8)]:
+        assert b.dg_instance_name(1, rows, n, k, g) == "contig_256x256", (rows, n, k)
