@@ -172,11 +172,11 @@ dg_status dg_grouped_gemm_fp8_masked_ex(const uint8_t *A, int a_format, const fl
  * division, rounded to the nearest value of `format`, ties to even, saturating at
  * +-FMAX.  So Q * S reproduces X to within half an fp8 step of each block's scale.
  *
- * Inputs: X rows x K (row-major, DEVICE), x_dtype DG_IN_F32 (16-byte aligned) or
- * DG_IN_BF16 (8-byte aligned); values must be finite (non-finite inputs give
- * unspecified codes and scales, never a fault).  K > 0, K % 128 == 0 (DG_ERR_SHAPE);
- * rows >= 0 (0: nothing to do).  Outputs (DEVICE, caller-owned, 4-byte aligned):
- * Q rows x K codes; S rows x K/128 (1x128) or ceil(rows/128) x K/128 (128x128) fp32.
+ * Inputs: X rows x K (row-major, DEVICE, 16-byte aligned), x_dtype DG_IN_F32 or
+ * DG_IN_BF16; values must be finite (non-finite inputs give unspecified codes and
+ * scales, never a fault).  K > 0, K % 128 == 0 (DG_ERR_SHAPE); rows >= 0 (0: nothing
+ * to do).  Outputs (DEVICE, caller-owned): Q rows x K codes (8-byte aligned); S rows x
+ * K/128 (1x128) or ceil(rows/128) x K/128 (128x128) fp32 (4-byte aligned).
  * Errors: DG_ERR_SHAPE, DG_ERR_FORMAT (format or x_dtype), DG_ERR_NULL, DG_ERR_ALIGN,
  * DG_ERR_DEVICE, DG_ERR_HIP, checked in that order.  Asynchronous on `stream`,
  * graph-capturable, deterministic. */

@@ -343,7 +343,7 @@ static dg_status quantize(int block128x128, const void* X, int x_dtype, uint8_t*
     return DG_ERR_FORMAT;
   if (rows == 0) return DG_OK;
   if (!X || !Q || !S) return DG_ERR_NULL;
-  if (!aligned(X, x_dtype == DG_IN_F32 ? 16 : 8) || !aligned(Q, 4) || !aligned(S, 4))
+  if (!aligned(X, 16) || !aligned(Q, 8) || !aligned(S, 4))
     return DG_ERR_ALIGN;
   int num_cus = 0;
   const dg_status st = check_device(&num_cus);

@@ -6,9 +6,9 @@
 // FMAX in fp32 (FMAX = 448 for E4M3, 57344 for E5M2; 1 for an all-zero block); each
 // code is x / scale (an IEEE fp32 division) rounded to the nearest fp8 value, ties to
 // even, saturating at +-FMAX.  Inputs are finite fp32 or bf16.  Memory-bound: every
-// thread moves 16 bytes of fp32 (8 of bf16) per load and writes 4 codes at once; the
-// per-element work is three fp32 operations for the quotient and the hardware's fp8
-// conversion.
+// load is 16 bytes (4 fp32 or 8 bf16 inputs) and the matching 4 or 8 codes go out in one
+// store; each lane keeps several loads in flight; the per-element work is three fp32
+// operations for the quotient and the hardware's fp8 conversion.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,21 +22,36 @@ __device__ __forceinline__ float fp8_max() {
   return FMT == kFmtE5M2 ? 57344.0f : 448.0f;
 }
 
+// E consecutive inputs as fp32 from one 16-byte load: E = 8 for bf16, 4 for fp32.
 template <bool BF16>
-__device__ __forceinline__ void load4(const void* X, int64_t i, float (&x)[4]) {
+struct In {
+  static constexpr int E = BF16 ? 8 : 4;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load16(const void* X, int64_t i, float (&x)[In<BF16>::E]) {
+  const uint4 u = *(const uint4*)((const uint8_t*)X + i * (BF16 ? 2 : 4));
   if (BF16) {
-    const uint2 u = *(const uint2*)((const uint16_t*)X + i);
-    x[0] = __uint_as_float(u.x << 16);
-    x[1] = __uint_as_float(u.x & 0xFFFF0000u);
-    x[2] = __uint_as_float(u.y << 16);
-    x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
   } else {
-    const float4 f = *(const float4*)((const float*)X + i);
-    x[0] = f.x;
-    x[1] = f.y;
-    x[2] = f.z;
-    x[3] = f.w;
+    x[0] = __uint_as_float(u.x);
+    x[1] = __uint_as_float(u.y);
+    x[2] = __uint_as_float(u.z);
+    x[3] = __uint_as_float(u.w);
   }
+}
+
+template <int E>
+__device__ __forceinline__ float amax_of(const float* x) {
+  float m = fabsf(x[0]);
+#pragma unroll
+  for (int e = 1; e < E; ++e) m = fmaxf(m, fabsf(x[e]));
+  return m;
 }
 
 // x / scale rounded to nearest fp32, from a correctly rounded reciprocal r = 1/scale:
@@ -53,7 +68,7 @@ __device__ __forceinline__ float div_by_scale(float x, float scale, float r) {
 // Four codes: the quotients saturated to +-FMAX, then converted by the hardware's
 // round-to-nearest-even fp8 conversion (OCP E4M3 / E5M2 on gfx950).
 template <int FMT>
-__device__ __forceinline__ uint32_t pack4(const float (&x)[4], float scale, float r) {
+__device__ __forceinline__ uint32_t pack4(const float* x, float scale, float r) {
   const float m = fp8_max<FMT>();
   float q[4];
 #pragma unroll
@@ -69,52 +84,79 @@ __device__ __forceinline__ uint32_t pack4(const float (&x)[4], float scale, floa
   return (uint32_t)v;
 }
 
-// 1x128 blocks: 32 lanes (half a wave) per block, 4 elements each; 8 blocks per
-// 256-thread workgroup.  Block b is row b / nkb, K block b % nkb, and its scale goes
-// to S[b] (S is rows x nkb).
+// E codes of one 16-byte load, stored with one 8- or 4-byte store.
+template <int FMT, bool BF16>
+__device__ __forceinline__ void store_codes(uint8_t* Q, int64_t i, const float* x, float scale,
+                                            float r) {
+  if (BF16)
+    *(uint2*)(Q + i) = make_uint2(pack4<FMT>(x, scale, r), pack4<FMT>(x + 4, scale, r));
+  else
+    *(uint32_t*)(Q + i) = pack4<FMT>(x, scale, r);
+}
+
+// 1x128 blocks: LPB = 128/E lanes per block (16 for bf16, 32 for fp32), each with one
+// 16-byte load; a wave holds 64/LPB blocks side by side and takes U such groups, issuing
+// all U loads before it reduces any block, so every lane keeps U loads in flight.  Block
+// b is row b / nkb, K block b % nkb, and its scale goes to S[b] (S is rows x nkb).  Loads
+// of blocks past the end re-read the last block; their stores are skipped.
 template <int FMT, bool BF16>
 __global__ void __launch_bounds__(256)
 quant_1x128_kernel(const void* X, uint8_t* Q, float* S, int64_t nblk, int nkb, int64_t K) {
-  const int64_t b = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
-  if (b >= nblk) return;                                   // uniform per half wave
-  const int l = threadIdx.x & 31;
-  const int64_t r = b / nkb;
-  const int64_t i = r * K + (b - r * nkb) * kBlockK + l * 4;
-  float x[4];
-  load4<BF16>(X, i, x);
-  float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+  constexpr int E = In<BF16>::E, LPB = kBlockK / E, BPW = 64 / LPB, U = 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = lane % LPB;
+  int64_t b[U], i[U];
+  float x[U][E];
 #pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
-  const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<FMT>();
-  const float rcp = 1.0f / scale;                          // correctly rounded
-  *(uint32_t*)(Q + i) = pack4<FMT>(x, scale, rcp);
-  if (l == 0) S[b] = scale;
+  for (int u = 0; u < U; ++u) {
+    b[u] = (wave * U + u) * BPW + lane / LPB;
+    const int64_t bb = b[u] < nblk ? b[u] : nblk - 1;
+    const int64_t r = bb / nkb;
+    i[u] = r * K + (bb - r * nkb) * kBlockK + l * E;
+    load16<BF16>(X, i[u], x[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float amax = amax_of<E>(x[u]);
+#pragma unroll
+    for (int off = LPB / 2; off >= 1; off >>= 1)
+      amax = fmaxf(amax, __shfl_xor(amax, off, LPB));
+    const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<FMT>();
+    const float rcp = 1.0f / scale;                        // correctly rounded
+    if (b[u] < nblk) {
+      store_codes<FMT, BF16>(Q, i[u], x[u], scale, rcp);
+      if (l == 0) S[b[u]] = scale;
+    }
+  }
 }
 
-// 128x128 blocks: one 256-thread workgroup per block; thread t covers columns
-// 4(t % 32) .. +3 of rows t / 32 + 8j, j = 0..15 (rows past the matrix are skipped).
+// 128x128 blocks: one 256-thread workgroup per block; thread t takes the E columns
+// starting at E(t % (128/E)) of rows t / (128/E) + R j, j = 0 .. 128/R - 1, where
+// R = 256 / (128/E) rows are covered per pass (rows past the matrix are skipped).
 template <int FMT, bool BF16>
 __global__ void __launch_bounds__(256)
 quant_128x128_kernel(const void* X, uint8_t* Q, float* S, int64_t rows, int nkb, int64_t K) {
+  constexpr int E = In<BF16>::E, TPR = kBlockK / E, R = 256 / TPR, J = kBlockK / R;
   __shared__ float wave_max[4];
   const int64_t b = blockIdx.x;
   const int64_t rb = b / nkb;
   const int kb = (int)(b - rb * nkb);
   const int t = threadIdx.x;
-  const int64_t col = (int64_t)kb * kBlockK + (t & 31) * 4;
-  const int64_t row0 = rb * kBlockK + (t >> 5);
-  float x[16][4];
+  const int64_t col = (int64_t)kb * kBlockK + (t % TPR) * E;
+  const int64_t row0 = rb * kBlockK + t / TPR;
+  float x[J][E];
   float amax = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int64_t r = row0 + 8 * j;
+  for (int j = 0; j < J; ++j) {
+    const int64_t r = row0 + R * j;
     if (r < rows) {
-      load4<BF16>(X, r * K + col, x[j]);
+      load16<BF16>(X, r * K + col, x[j]);
     } else {
-      x[j][0] = x[j][1] = x[j][2] = x[j][3] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[j][e] = 0.0f;
     }
-    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(x[j][0]), fabsf(x[j][1])),
-                             fmaxf(fabsf(x[j][2]), fabsf(x[j][3]))));
+    amax = fmaxf(amax, amax_of<E>(x[j]));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
@@ -125,18 +167,20 @@ quant_128x128_kernel(const void* X, uint8_t* Q, float* S, int64_t rows, int nkb,
   const float rcp = 1.0f / scale;                          // correctly rounded
   if (t == 0) S[b] = scale;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int64_t r = row0 + 8 * j;
-    if (r < rows) *(uint32_t*)(Q + r * K + col) = pack4<FMT>(x[j], scale, rcp);
+  for (int j = 0; j < J; ++j) {
+    const int64_t r = row0 + R * j;
+    if (r < rows) store_codes<FMT, BF16>(Q, r * K + col, x[j], scale, rcp);
   }
 }
 
 template <int FMT, bool BF16>
 void launch_1x128(const void* X, uint8_t* Q, float* S, int64_t rows, int64_t K,
                   hipStream_t stream) {
+  constexpr int E = In<BF16>::E, BPW = 64 / (kBlockK / E), U = 4;
   const int nkb = (int)(K / kBlockK);
   const int64_t nblk = rows * nkb;
-  hipLaunchKernelGGL((quant_1x128_kernel<FMT, BF16>), dim3((unsigned)((nblk + 7) / 8)),
+  const int64_t per_wg = 4 * U * BPW;                      // blocks per 256-thread workgroup
+  hipLaunchKernelGGL((quant_1x128_kernel<FMT, BF16>), dim3((unsigned)((nblk + per_wg - 1) / per_wg)),
                      dim3(256), 0, stream, X, Q, S, nblk, nkb, K);
 }
 

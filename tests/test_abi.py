@@ -97,8 +97,9 @@ def test_quantize_validation_codes(lib):
         assert f(None, 0, A16, A4, 0, 128, 1, None) == 0      # nothing to do
         assert f(None, 0, A16, A4, 64, 128, 0, None) == 1
         assert f(A16, 1, A16, None, 64, 128, 0, None) == 1
-        assert f(A16 + 8, 0, A16, A4, 64, 128, 0, None) == 3  # fp32 input: 16 bytes
-        assert f(A16, 0, A16 + 2, A4, 64, 128, 0, None) == 3
+        assert f(A16 + 8, 0, A16, A4, 64, 128, 0, None) == 3  # 16-byte input loads
+        assert f(A16 + 8, 1, A16, A4, 64, 128, 0, None) == 3  # bf16 too
+        assert f(A16, 0, A16 + 4, A4, 64, 128, 0, None) == 3  # 8-byte code stores
         assert f(A16, 0, A16, A4 + 1, 64, 128, 0, None) == 3
 
 
@@ -147,9 +148,9 @@ def test_device_check_without_gpu(lib):
     need = b.dg_workspace_bytes(0, 64, 256, 512, 1)
     assert lib.dg_gemm_fp8_nt(A16, A4, A16, A4, A16, 64, 256, 512, A16, need, None) == 5
     assert lib.dg_gemm_fp8_nt(A16, A4, A16, A4, A16, 4096, 4096, 512, None, 0, None) == 5
-    # bf16 input needs only 8-byte alignment: validation passes, the device check fails
-    assert lib.dg_quantize_fp8_1x128(A16 + 8, 1, A16, A4 + 4, 64, 128, 1, None) == 5
-    assert lib.dg_quantize_fp8_128x128(A16 + 8, 1, A16, A4 + 4, 64, 128, 1, None) == 5
+    # aligned fake pointers pass validation; the device check then fails
+    assert lib.dg_quantize_fp8_1x128(A16, 1, A16 + 8, A4 + 4, 64, 128, 1, None) == 5
+    assert lib.dg_quantize_fp8_128x128(A16, 1, A16 + 8, A4 + 4, 64, 128, 1, None) == 5
 
 
 def test_instance_selection_is_host_logic(lib):
