@@ -99,12 +99,12 @@ double tile_cost(int64_t rows, int64_t N, int64_t groups, int bm, int bn, double
   return (double)rounds * bm * bn / eff;
 }
 
-// A stream-K instance holds every row in one tile and needs one arrival counter per
-// (column tile, wave).
-bool stream_fits(const Instance* in, int64_t rows, int64_t N) {
-  if (in->mode == dg::kModeStream)
-    return rows <= in->bm;
-  return true;
+// A dense stream-K instance holds every row in one tile; the masked one schedules at
+// most 64 groups (one per lane of a wave).
+bool stream_fits(const Instance* in, int64_t rows, int64_t N, int64_t G) {
+  if (in->mode != dg::kModeStream) return true;
+  if (in->kind == dg::kMasked) return G <= 64;
+  return rows <= in->bm;
 }
 
 // Instance selection: the heuristic that maps a problem to a build-time instance.
@@ -116,7 +116,7 @@ const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_
   const char* forced = getenv("DG_FORCE_INSTANCE");
   if (forced && *forced) {
     const Instance* f = find_instance(forced, fa, fb);
-    if (f && f->kind == kind && stream_fits(f, rows_or_cap, N)) return f;
+    if (f && f->kind == kind && stream_fits(f, rows_or_cap, N, G)) return f;
   }
   const char* name = nullptr;
   const int64_t groups = kind == dg::kMasked ? G : 1;
@@ -156,7 +156,17 @@ const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_
           name = find_instance(buf, fa, fb)->name;
         }
       }
-      if (kind == dg::kMasked && rows_or_cap <= 64) name = "masked_64x128";
+      const int64_t tiles128 = cdiv(N, 128) * G;
+      if (kind == dg::kMasked && rows_or_cap <= 128 && G <= 64 && tiles128 < kAssumedCUs) {
+        // every group fits one 128-row tile but the tiles are fewer than the CUs: split-K
+        // over the groups' column tiles and K blocks (scheduled on the device from
+        // masked_m) spreads the work over every CU (with a tile per CU or more, the tiled
+        // kernel is faster: no hand-off)
+        const int64_t nkb = K / dg::kBlockK;
+        name = tiles128 * nkb >= 16 * kAssumedCUs ? "masked_128x128_stream" : "masked_128x64_stream";
+      } else if (kind == dg::kMasked && rows_or_cap <= 64) {
+        name = "masked_64x128";      // more than 64 groups of at most 64 rows
+      }
       break;
     }
     default:

@@ -562,10 +562,84 @@ gemm_fp8_kernel(GemmArgs p) {
 // workgroup per CU (the LDS budget admits no second), so all contributors are resident
 // and every wait ends; the wait is bounded all the same.  A workgroup holds at most two
 // shared tiles: the first and the last of its range.
+// Where the stream-K iterations of the masked form live.  Lane l of every wave holds
+// group l's row tiles under its masked_m (clamped to [0, cap]) and, scanned over the
+// lanes, the first tile of group l + 1 (the groups' tiles are row-major: all column tiles
+// of a group's first row tile, then its second row tile, ...).  At most 64 groups.
+struct MaskedPlan {
+  int mm;          // this lane's group: rows under masked_m
+  int rt;          // its row tiles
+  int incl;        // tiles of groups 0 .. lane
+  int total;       // tiles of all groups
+};
+
+template <class C>
+__device__ __forceinline__ MaskedPlan masked_plan(const GemmArgs& p, int lane) {
+  MaskedPlan m;
+  int v = lane < p.G ? p.masked_m[lane] : 0;
+  v = v < 0 ? 0 : (v > p.rows ? p.rows : v);
+  m.mm = v;
+  m.rt = (v + C::BM - 1) / C::BM;
+  int incl = m.rt * p.tiles_n;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += u;
+  }
+  m.incl = incl;
+  m.total = __builtin_amdgcn_readlane(incl, 63);
+  return m;
+}
+
+// A position in the masked form's tile sequence: group g, row tile r, column tile n.
+struct MaskedCursor {
+  int g, r, n;
+};
+
+// The cursor of tile t (t < total): its group is the number of groups whose tiles all
+// come before t.
+template <class C>
+__device__ __forceinline__ MaskedCursor masked_seek(const MaskedPlan& m, int tiles_n, int t) {
+  MaskedCursor c;
+  c.g = (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(m.incl <= t));
+  const int first = __builtin_amdgcn_readlane(m.incl, c.g) -
+                    __builtin_amdgcn_readlane(m.rt, c.g) * tiles_n;
+  const int o = t - first;
+  c.r = o / tiles_n;
+  c.n = o - c.r * tiles_n;
+  return c;
+}
+
+// The next tile after c (only called while there is one).
+template <class C>
+__device__ __forceinline__ void masked_next(const MaskedPlan& m, int tiles_n, MaskedCursor& c) {
+  if (++c.n < tiles_n) return;
+  c.n = 0;
+  if (++c.r < __builtin_amdgcn_readlane(m.rt, c.g)) return;
+  c.r = 0;
+  // the next group with at least one row tile
+  const uint64_t later = __builtin_amdgcn_ballot_w64(m.rt > 0) & ~((2ull << c.g) - 1);
+  c.g = later ? (int)__builtin_ctzll(later) : 64;
+}
+
+// Tile fields of the copy / math context for cursor c.
+template <class C>
+__device__ __forceinline__ void masked_tile(const GemmArgs& p, const MaskedPlan& m,
+                                            const MaskedCursor& c, TileCtx& x) {
+  const int g = c.g < 64 ? c.g : 0;
+  const int mm = __builtin_amdgcn_readlane(m.mm, g);
+  x.a_row0 = g * p.rows + c.r * C::BM;
+  x.rows = min(C::BM, mm - c.r * C::BM);
+  x.Bg = p.B + (size_t)g * p.N * p.K;
+  x.sBg = p.sB + (size_t)g * p.nnb * p.nkb;
+  x.n0 = c.n * C::BN;
+  x.nb_first = x.n0 / kBlockK;
+}
+
 template <class C>
 __device__ __forceinline__ long stream_start(long g, long W, long G) { return g * W / G; }
 
-template <class C>
+template <int KIND, class C>
 __global__ void __launch_bounds__(C::NT)
 gemm_fp8_stream_kernel(GemmArgs p) {
   constexpr int TI = C::TI, TJ = C::TJ, STAGES = C::STAGES;
@@ -581,11 +655,22 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   const int q = lane >> 4;
   const int l16 = lane & 15;
   const int nkb = p.nkb;
-  const long W = (long)p.num_tiles * nkb;
-  const long G = gridDim.x;
+  // masked form: the tiles under masked_m, counted on the device (the grid is sized for
+  // the capacity, so some workgroups may get no iterations at all)
+  MaskedPlan mp;
+  int num_tiles = p.num_tiles;
+  if (KIND == kMasked) {
+    mp = masked_plan<C>(p, lane);
+    num_tiles = mp.total;
+  }
+  const long W = (long)num_tiles * nkb;
+  // the iterations are split over the first min(grid, W) workgroups, so that each of them
+  // has at least one (the contributor arithmetic of the reduction relies on it); the
+  // others have nothing to do
+  const long G = W < (long)gridDim.x ? W : (long)gridDim.x;
   const long g = blockIdx.x;
-  const long i_begin = stream_start<C>(g, W, G);
-  const long i_end = stream_start<C>(g + 1, W, G);
+  const long i_begin = g < G ? stream_start<C>(g, W, G) : 0;
+  const long i_end = g < G ? stream_start<C>(g + 1, W, G) : 0;
   const int t_first = (int)(i_begin / nkb);
 
   TileCtx cn, cc;
@@ -622,17 +707,28 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   const int n_iter = (int)(i_end - i_begin);
   int tn = t_first, kbn = (int)(i_begin - (long)t_first * nkb), sn = 0;   // next copy
   int tc = tn, kbc = kbn, sc = 0, in_tile = 0;                              // next math
+  MaskedCursor mn = {0, 0, 0}, mc = {0, 0, 0};      // masked form: the same two tiles
+  if (KIND == kMasked && n_iter > 0) {
+    mn = masked_seek<C>(mp, p.tiles_n, t_first);
+    mc = mn;
+  }
   int shared_tile[2] = {-1, -1};
+  int seg_row0[2] = {0, 0}, seg_rows[2] = {0, 0}, seg_n0[2] = {0, 0};  // where they go
   for (int step = 1 - STAGES; step < n_iter; ++step) {
     if (step >= 0) {
       wait_stage_copies<C, STAGES - 2>(wave, min(STAGES - 2, n_iter - 1 - step));
       stage_barrier();
     }
     const bool issue = step + STAGES - 1 < n_iter;
-    cn.n0 = tn * C::BN;
-    cn.nb_first = cn.n0 / kBlockK;
-    cc.n0 = tc * C::BN;
-    cc.nb_first = cc.n0 / kBlockK;
+    if (KIND == kMasked) {
+      masked_tile<C>(p, mp, mn, cn);
+      masked_tile<C>(p, mp, mc, cc);
+    } else {
+      cn.n0 = tn * C::BN;
+      cn.nb_first = cn.n0 / kBlockK;
+      cc.n0 = tc * C::BN;
+      cc.nb_first = cc.n0 / kBlockK;
+    }
     kb_step<C>(smem + sn * C::STAGE_BYTES, smem + sc * C::STAGE_BYTES, cn, issue, kbn, cc,
                step >= 0, acc);
     if (issue) {
@@ -640,6 +736,7 @@ gemm_fp8_stream_kernel(GemmArgs p) {
       if (++kbn == nkb) {
         kbn = 0;
         ++tn;
+        if (KIND == kMasked && step + STAGES < n_iter) masked_next<C>(mp, p.tiles_n, mn);
       }
     }
     if (step < 0) continue;
@@ -651,10 +748,13 @@ gemm_fp8_stream_kernel(GemmArgs p) {
 
     // tile tc ends here for this workgroup
     if (in_tile == nkb) {
-      store_tile_bf16<C>(acc, p.C, p.N, 0, p.rows, tc * C::BN, wm, wn, q, l16);
+      store_tile_bf16<C>(acc, p.C, p.N, cc.a_row0, cc.rows, cc.n0, wm, wn, q, l16);
     } else {
       const int seg = tc == t_first ? 0 : 1;
       shared_tile[seg] = tc;
+      seg_row0[seg] = cc.a_row0;
+      seg_rows[seg] = cc.rows;
+      seg_n0[seg] = cc.n0;
       const int base = (int)(((g * 2 + seg) * C::W + wave) * WAVE_SLOT) * 4;
 #pragma unroll
       for (int i = 0; i < TI; ++i)
@@ -669,6 +769,7 @@ gemm_fp8_stream_kernel(GemmArgs p) {
 #pragma unroll
       for (int j = 0; j < TJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     ++tc;
+    if (KIND == kMasked && step < n_iter - 1) masked_next<C>(mp, p.tiles_n, mc);
     in_tile = 0;
   }
 
@@ -685,7 +786,11 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   constexpr int CB = 8;                                    // contributors per fetch
   constexpr int kPastBuffer = 0x7FFFFF00;                  // beyond part_rsrc's range
   const int t_last = (int)((i_end - 1) / nkb);
+  const int sel = shared_tile[1] >= 0 ? 1 : 0;
   const int t = shared_tile[1] >= 0 ? shared_tile[1] : (shared_tile[0] == t_last ? t_last : -1);
+  const int t_row0 = sel ? seg_row0[1] : seg_row0[0];
+  const int t_rows = sel ? seg_rows[1] : seg_rows[0];
+  const int t_n0 = sel ? seg_n0[1] : seg_n0[0];
   if (t >= 0) {
     const long x0 = (long)t * nkb, x1 = x0 + nkb - 1;
     const long g_first = ((x0 + 1) * G + W - 1) / W - 1;
@@ -758,9 +863,9 @@ gemm_fp8_stream_kernel(GemmArgs p) {
         const int fi = rem / TJ, fj = rem - fi * TJ;
         const int swm = sw / C::WAVES_N, swn = sw - swm * C::WAVES_N;
         const int row = swm * C::WM + 16 * fi + l16;
-        const int col = t * C::BN + swn * C::WN + 16 * fj + 4 * q;
-        if (row < p.rows) {
-          uint16_t* dst = p.C + (size_t)row * p.N;
+        const int col = t_n0 + swn * C::WN + 16 * fj + 4 * q;
+        if (row < t_rows) {
+          uint16_t* dst = p.C + (size_t)(t_row0 + row) * p.N;
           if (((p.N & 3) == 0) && col + 3 < p.N) {
             const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
             const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
@@ -776,9 +881,9 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   }
 }
 
-template <class C>
+template <int KIND, class C>
 void launch_stream(const GemmArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_fp8_stream_kernel<C>), dim3(grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((gemm_fp8_stream_kernel<KIND, C>), dim3(grid), dim3(C::NT), 0, stream, a);
 }
 
 // persistent stream grid: one workgroup per CU (at most kStreamGrid), never more
@@ -820,31 +925,33 @@ template <int FA, int FB> using Str128n64 = Cfg<128, 64, 2, 4, 6, true, FA, FB>;
 #define DG_INST1(NAME, KIND, C, FA, FB)                                                   \
   Instance { NAME, KIND, C::BM, C::BN, kModeTiled, C::NT, FA, FB, grid_persistent,        \
              launch<KIND, C> }
-#define DG_STREAM1(NAME, C, FA, FB)                                                        \
-  Instance { NAME, kDense, C::BM, C::BN, kModeStream, C::NT, FA, FB, grid_stream,         \
-             launch_stream<C> }
+#define DG_STREAM1(NAME, KIND, C, FA, FB)                                                  \
+  Instance { NAME, KIND, C::BM, C::BN, kModeStream, C::NT, FA, FB, grid_stream,           \
+             launch_stream<KIND, C> }
 #define DG_INST(NAME, KIND, T)                                                             \
   DG_INST1(NAME, KIND, T<0 COMMA 0>, 0, 0), DG_INST1(NAME, KIND, T<1 COMMA 1>, 1, 1),      \
       DG_INST1(NAME, KIND, T<0 COMMA 1>, 0, 1), DG_INST1(NAME, KIND, T<1 COMMA 0>, 1, 0)
-#define DG_STREAM(NAME, T)                                                                 \
-  DG_STREAM1(NAME, T<0 COMMA 0>, 0, 0), DG_STREAM1(NAME, T<1 COMMA 1>, 1, 1),              \
-      DG_STREAM1(NAME, T<0 COMMA 1>, 0, 1), DG_STREAM1(NAME, T<1 COMMA 0>, 1, 0)
+#define DG_STREAM(NAME, KIND, T)                                                           \
+  DG_STREAM1(NAME, KIND, T<0 COMMA 0>, 0, 0), DG_STREAM1(NAME, KIND, T<1 COMMA 1>, 1, 1),  \
+      DG_STREAM1(NAME, KIND, T<0 COMMA 1>, 0, 1), DG_STREAM1(NAME, KIND, T<1 COMMA 0>, 1, 0)
 #define COMMA ,
 
 static const Instance kInstances[] = {
     DG_INST("dense_256x256", kDense, Big),
     DG_INST("dense_256x224", kDense, Big224),
     DG_INST("dense_128x128", kDense, Mid),
-    DG_STREAM("dense_64x128_stream", Str64),
-    DG_STREAM("dense_64x64_stream", Str64n64),
-    DG_STREAM("dense_128x128_stream", Str128),
-    DG_STREAM("dense_128x64_stream", Str128n64),
+    DG_STREAM("dense_64x128_stream", kDense, Str64),
+    DG_STREAM("dense_64x64_stream", kDense, Str64n64),
+    DG_STREAM("dense_128x128_stream", kDense, Str128),
+    DG_STREAM("dense_128x64_stream", kDense, Str128n64),
     DG_INST("contig_256x256", kContiguous, BigC),
     DG_INST("contig_256x224", kContiguous, Big224C),
     DG_INST("contig_128x128", kContiguous, Mid),
     DG_INST("masked_256x256", kMasked, Big),
     DG_INST("masked_128x128", kMasked, Mid),
     DG_INST("masked_64x128", kMasked, Small),
+    DG_STREAM("masked_128x128_stream", kMasked, Str128),
+    DG_STREAM("masked_128x64_stream", kMasked, Str128n64),
 };
 
 const Instance* instances(int* count) {

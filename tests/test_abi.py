@@ -180,3 +180,20 @@ def test_tiled_selection_uses_measured_tile_efficiency(lib):
     for rows, n, k, g in [(32768, 4096, 7168, 4), (30592, 4096, 7168, 8),
                           (32768, 7168, 2048, 8), (24448, 7168, 2048, 8)]:
         assert b.dg_instance_name(1, rows, n, k, g) == "contig_256x256", (rows, n, k)
+
+
+def test_masked_selection(lib):
+    """Masked calls whose groups each fit one 128-row tile (at most 64 groups) and whose
+    column tiles are fewer than the CUs take the split-K instances that schedule on the
+    device; otherwise the tiled ones."""
+    from moe_grouped_gemm_lhs_amd import binding as b
+    assert b.dg_instance_name(2, 128, 4096, 7168, 4) == "masked_128x128_stream"
+    assert b.dg_instance_name(2, 128, 4096, 7168, 8) == "masked_128x128"     # 256 tiles
+    assert b.dg_instance_name(2, 64, 4096, 7168, 32) == "masked_64x128"
+    assert b.dg_instance_name(2, 100, 256, 512, 2) == "masked_128x64_stream"
+    assert b.dg_instance_name(2, 64, 512, 512, 100) == "masked_64x128"
+    assert b.dg_instance_name(2, 256, 4096, 7168, 4) == "masked_128x128"
+    assert b.dg_instance_name(2, 128, 4096, 7168, 65).startswith("masked_") and \
+        "stream" not in b.dg_instance_name(2, 128, 4096, 7168, 65)
+    assert b.dg_workspace_bytes(2, 128, 4096, 7168, 4) > 0
+    assert b.dg_workspace_bytes(2, 256, 4096, 7168, 4) == 0

@@ -125,6 +125,53 @@ def test_stream_k_shared_tiles(M, N, K, monkeypatch):
     monkeypatch.delenv("DG_FORCE_INSTANCE")
 
 
+MASKED_STREAM_INSTANCES = ["masked_128x128_stream", "masked_128x64_stream"]
+
+
+@pytest.mark.parametrize("G,cap,N,K,mm", [
+    (3, 200, 400, 384, [200, 37, 0]),                      # ragged rows, an empty group
+    (6, 96, 300, 512, [0, 96, 1, 95, -5, 103]),            # counts outside [0, cap]
+    (2, 128, 130, 128 * 60, [128, 70]),                    # tiles shared by many workgroups
+    (64, 16, 256, 1024, None),                             # the 64-group limit
+    (4, 512, 256, 2048, [512, 0, 300, 129]),               # several row tiles per group
+])
+def test_masked_stream_k(G, cap, N, K, mm, monkeypatch):
+    """Split-K masked instances (the schedule is built on the device from masked_m): every
+    written row within tolerance, every other row untouched, the workspace left zero
+    filled after each of two calls; all-zero counts write nothing."""
+    from moe_grouped_gemm_lhs_amd import binding as b
+    if mm is None:
+        mm = np.random.default_rng(G + cap).integers(0, cap + 1, size=G)
+    p = I.make_masked(G, cap, N, K, seed=G * 7 + cap, masked_m=mm)
+    ops = gu.device_operands(p)
+    c_ref = gu.oracle_full(p)
+    w = np.repeat(gu.written_rows(p)[:, None], N, axis=1)
+    for name in MASKED_STREAM_INSTANCES:
+        monkeypatch.setenv("DG_FORCE_INSTANCE", name)
+        assert b.dg_instance_name(2, cap, N, K, G) == name
+        ws = torch.zeros(b.dg_workspace_bytes(2, cap, N, K, G), dtype=torch.uint8,
+                         device=gu.DEV)
+        for rep in range(2):
+            gu.say(f"[case] {name} G={G} cap={cap} N={N} K={K} call {rep}")
+            mmv = torch.from_numpy(np.asarray(p.masked_m, np.int32)).to(gu.DEV)
+            C = torch.from_numpy(np.full((G * cap, N), SENTINEL, np.uint16).view(np.int16)
+                                 ).to(gu.DEV).view(torch.bfloat16)
+            b.dg_grouped_gemm_fp8_masked(*ops[:4], mmv, C.view(G, cap, N), workspace=ws)
+            torch.cuda.synchronize()
+            c_gpu = C.view(torch.int16).cpu().numpy().view(np.uint16)
+            assert_within_tolerance(c_gpu, c_ref, w, f"{name} masked G={G}")
+            assert np.all(c_gpu[~w] == SENTINEL), f"{name}: rows past masked_m written"
+            assert not ws.cpu().numpy().any(), f"{name}: workspace not left zero filled"
+        gu.say(f"[case] {name} all-zero counts")
+        z = torch.zeros(G, dtype=torch.int32, device=gu.DEV)
+        C = torch.from_numpy(np.full((G * cap, N), SENTINEL, np.uint16).view(np.int16)
+                             ).to(gu.DEV).view(torch.bfloat16)
+        b.dg_grouped_gemm_fp8_masked(*ops[:4], z, C.view(G, cap, N), workspace=ws)
+        torch.cuda.synchronize()
+        assert np.all(C.view(torch.int16).cpu().numpy().view(np.uint16) == SENTINEL)
+    monkeypatch.delenv("DG_FORCE_INSTANCE")
+
+
 # ------------------------------------------------------- E5M2 operands (either or both)
 FMT_PAIRS = [("e5m2", "e5m2"), ("e4m3", "e5m2"), ("e5m2", "e4m3")]
 
