@@ -125,10 +125,13 @@ const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_
       // decode-shaped (all rows in one tile): persistent stream-K over the column tiles
       // and K blocks
       if (rows_or_cap <= 128) {
-        // 128-column tiles when every CU gets long runs of K blocks; 64-column tiles
-        // otherwise (fewer contributors per shared tile)
+        // 128-column tiles (half the re-reads of A per byte of B) unless their grid would
+        // leave more than a quarter of the CUs idle; 64-column tiles then (twice the
+        // tiles; measured: 64x24576x1536 17.5 -> 12.1 us and 128x4096x7168 18.9 -> 17.4
+        // us with 128 columns; 2112x7168 and 7168x2048 keep 64)
         const int64_t tiles128 = cdiv(N, 128), nkb = K / dg::kBlockK;
-        const bool wide = tiles128 * nkb >= 16 * kAssumedCUs;
+        const bool wide =
+            4 * dg::stream_grid(tiles128, nkb, kAssumedCUs) >= 3 * kAssumedCUs;
         if (rows_or_cap <= 64)
           name = wide ? "dense_64x128_stream" : "dense_64x64_stream";
         else

@@ -20,6 +20,22 @@ constexpr int kStreamGrid = 256;
 // fragment whose wait runs out is stored as NaN.
 constexpr int kSpinLimit = 1 << 16;
 
+// Workgroups of a dense stream-K launch over `tiles` output tiles of `nkb` K blocks on
+// a grid of at most `g` (min(CUs, kStreamGrid)): whole tiles dealt out evenly when that
+// keeps at least 70% of the grid, so that no tile is shared and nothing is reduced;
+// otherwise at least 8 iterations per workgroup, where a shared tile's hand-off costs
+// more than the shorter loop saves; never more workgroups than iterations.
+inline long stream_grid(long tiles, long nkb, long g) {
+  const long work = tiles * nkb;
+  if (work <= g) return work;
+  for (long k = 1; k <= tiles; ++k) {
+    if (tiles % k != 0 || tiles / k > g) continue;
+    if (10 * (tiles / k) >= 7 * g) return tiles / k;
+    break;
+  }
+  return work / 8 < g ? (work / 8 > 0 ? work / 8 : 1) : g;
+}
+
 // Instance modes.
 constexpr int kModeTiled = 0;    // one output tile per work item
 constexpr int kModeStream = 2;   // persistent stream-K over (tile, K block) iterations

@@ -886,24 +886,17 @@ void launch_stream(const GemmArgs& a, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_fp8_stream_kernel<KIND, C>), dim3(grid), dim3(C::NT), 0, stream, a);
 }
 
-// persistent stream grid: one workgroup per CU (at most kStreamGrid), never more
-// workgroups than iterations.  Dense calls (whose tile count the host knows) prefer,
-// when it keeps at least 70% of the CUs, a grid that deals out whole tiles evenly, so
-// that no tile is shared and nothing is reduced (128x24576x1536: 24.5 -> 21.8 us on 192
-// workgroups); otherwise they give each workgroup at least 8 iterations, where a shared
-// tile's hand-off costs more than the shorter loop saves (128x2112x7168 on 231
-// workgroups: 14.9 -> 13.1 us).  The masked form's tiles are counted on the device.
+// persistent stream grid: one workgroup per CU (at most kStreamGrid); dense calls follow
+// stream_grid (128x24576x1536 on 192 workgroups shares no tile: 24.5 -> 21.8 us;
+// 128x2112x7168 on 231: 14.9 -> 13.1 us); the masked form's tiles are counted on the
+// device, so its grid covers the capacity
 int grid_stream(const GemmArgs& a, int num_cus) {
-  const long work = (long)a.num_tiles * a.nkb;
   const long g = num_cus < kStreamGrid ? num_cus : kStreamGrid;
-  if (work <= g) return (int)work;
-  if (a.masked_m) return (int)g;
-  for (long k = 1; k <= a.num_tiles; ++k) {
-    if (a.num_tiles % k != 0 || a.num_tiles / k > g) continue;
-    if (10 * (a.num_tiles / k) >= 7 * g) return (int)(a.num_tiles / k);
-    break;
+  if (a.masked_m) {
+    const long work = (long)a.num_tiles * a.nkb;
+    return (int)(work < g ? work : g);
   }
-  return (int)(work / 8 < g ? (work / 8 > 0 ? work / 8 : 1) : g);
+  return (int)stream_grid(a.num_tiles, a.nkb, g);
 }
 
 template <int KIND, class C>
