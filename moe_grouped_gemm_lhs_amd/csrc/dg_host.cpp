@@ -145,9 +145,11 @@ const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_
       // eff: measured throughput per unit of tile area, relative to 256x256.  The 256x224
       // tile does less MFMA work per K block for about the same fixed costs (0.88); the
       // contiguous form's 256x224 build also copies from every wave (0.75).
+      // The dense 256x160 tile (for N near 2048: one round of tiles) runs at 0.80.
       const double eff224 = kind == dg::kContiguous ? 0.75 : 0.88;
       struct Opt { const char* suffix; int bm, bn; double eff; } opts[] = {
-          {"256x256", 256, 256, 1.0}, {"256x224", 256, 224, eff224}, {"128x128", 128, 128, 0.6}};
+          {"256x256", 256, 256, 1.0}, {"256x224", 256, 224, eff224}, {"256x160", 256, 160, 0.80},
+          {"128x128", 128, 128, 0.6}};
       double best = 1e300;
       static char buf[64];
       for (const Opt& o : opts) {

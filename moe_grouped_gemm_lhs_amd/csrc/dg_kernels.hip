@@ -912,6 +912,7 @@ int grid_persistent(const GemmArgs& a, int num_cus) {
 // Tile shapes, each built for the four operand-format pairs (FA, FB).
 template <int FA, int FB> using Big = Cfg<256, 256, 4, 2, 2, false, FA, FB, 4>;     // 8 waves, 64x128 each
 template <int FA, int FB> using Big224 = Cfg<256, 224, 4, 2, 2, false, FA, FB, 4>;  // non-power-of-two N tile
+template <int FA, int FB> using Big160 = Cfg<256, 160, 4, 2, 2, false, FA, FB, 4>;  // for N near 2048
 // the contiguous form keeps more per-tile state: its 256x224 tile has no registers to
 // spare for the copy waves' doubled copy set, so all of its waves copy
 template <int FA, int FB> using BigC = Cfg<256, 256, 4, 2, 2, false, FA, FB, 4>;
@@ -944,6 +945,7 @@ template <int FA, int FB> using Str128n64 = Cfg<128, 64, 2, 4, 6, true, FA, FB>;
 static const Instance kInstances[] = {
     DG_INST("dense_256x256", kDense, Big),
     DG_INST("dense_256x224", kDense, Big224),
+    DG_INST("dense_256x160", kDense, Big160),
     DG_INST("dense_128x128", kDense, Mid),
     DG_STREAM("dense_64x128_stream", kDense, Str64),
     DG_STREAM("dense_64x64_stream", kDense, Str64n64),

@@ -169,10 +169,11 @@ def test_instance_selection_is_host_logic(lib):
 
 def test_tiled_selection_uses_measured_tile_efficiency(lib):
     """The tile-shape heuristic (full rounds of tiles over 256 CUs, divided by each shape's
-    measured per-area efficiency) on the bench's prefill and contiguous shapes: 256x224
-    only where it saves a whole round of tiles, never for the contiguous form."""
+    measured per-area efficiency) on the bench's prefill and contiguous shapes: the
+    narrower 256x224 / 256x160 tiles only where they save a whole round of tiles, never
+    for the contiguous form."""
     from moe_grouped_gemm_lhs_amd import binding as b
-    dense = {(2112, 7168): "dense_256x224", (24576, 1536): "dense_256x256",
+    dense = {(2112, 7168): "dense_256x160", (24576, 1536): "dense_256x256",
              (32768, 512): "dense_256x256", (7168, 16384): "dense_256x224",
              (4096, 7168): "dense_256x256", (7168, 2048): "dense_256x224"}
     for (n, k), name in dense.items():
