@@ -102,11 +102,16 @@ __device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t r, int off, void* l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// bf16 rounding (nearest, ties to even) by the hardware's packed conversion
+// (v_cvt_pk_bf16_f32): bit-identical to the software rounding on finite values, ties,
+// denormals and overflow to infinity (4M-value check on gfx950); NaN stays a NaN.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -413,13 +418,13 @@ __device__ __forceinline__ void store_tile_bf16(const v4f (&acc)[C::TI][C::TJ], 
       const int n = n0 + wn * C::WN + 16 * j + 4 * q;
       const v4f v = acc[i][j];
       if (((N & 3) == 0) && n + 3 < N) {
-        const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-        const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+        const uint32_t lo = bf16x2_rne(v[0], v[1]);
+        const uint32_t hi = bf16x2_rne(v[2], v[3]);
         *(uint2*)(crow + n) = make_uint2(lo, hi);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (n + e < N) crow[n + e] = (uint16_t)bf16_rne_bits(v[e]);
+          if (n + e < N) crow[n + e] = bf16_rne(v[e]);
       }
     }
   }
@@ -526,13 +531,13 @@ gemm_fp8_kernel(GemmArgs p) {
           const int n = tr.n0 + wn * WN + 16 * j + 4 * q;
           const v4f v = acc[i][j];
           if (((p.N & 3) == 0) && n + 3 < p.N) {
-            const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-            const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+            const uint32_t lo = bf16x2_rne(v[0], v[1]);
+            const uint32_t hi = bf16x2_rne(v[2], v[3]);
             *(uint2*)(crow + n) = make_uint2(lo, hi);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (n + e < p.N) crow[n + e] = (uint16_t)bf16_rne_bits(v[e]);
+              if (n + e < p.N) crow[n + e] = bf16_rne(v[e]);
           }
         }
       }
@@ -867,13 +872,13 @@ gemm_fp8_stream_kernel(GemmArgs p) {
         if (row < t_rows) {
           uint16_t* dst = p.C + (size_t)(t_row0 + row) * p.N;
           if (((p.N & 3) == 0) && col + 3 < p.N) {
-            const uint32_t lo = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
-            const uint32_t hi = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+            const uint32_t lo = bf16x2_rne(v[0], v[1]);
+            const uint32_t hi = bf16x2_rne(v[2], v[3]);
             *(uint2*)(dst + col) = make_uint2(lo, hi);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (col + e < p.N) dst[col + e] = (uint16_t)bf16_rne_bits(v[e]);
+              if (col + e < p.N) dst[col + e] = bf16_rne(v[e]);
           }
         }
       }
