@@ -61,6 +61,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// s_waitcnt lgkmcnt(0): this wave's LDS accesses are complete (vmcnt untouched).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Wait until at most `ahead` stages (PER loads each) of this wave are still in flight.
 template <int PER, int A>
 __device__ __forceinline__ void wait_stages_ahead(int ahead) {
@@ -515,30 +518,47 @@ gemm_fp8_kernel(GemmArgs p) {
       }
 
       // ---------------------------------------------------------------- epilogue
+      // The tile goes out through LDS, free once every wave is past the last stage: the
+      // waves write their fragments there as bf16 rows, then the workgroup stores whole
+      // row segments, 16 bytes per lane with consecutive lanes along a row (straight
+      // from the MFMA layout a store instruction would cover 16 rows x 32 bytes).  Rows
+      // are padded by 16 bytes so that the fragment writes spread over the banks.
+      constexpr int ROW_BYTES = C::BN * 2 + 16;
+      constexpr int CHUNKS = C::BN / 8;                    // 16-byte chunks per row
+      static_assert(C::BM * ROW_BYTES <= STAGES * C::STAGE_BYTES, "epilogue staging");
+      stage_barrier();                                      // the stages are free
 #pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const int ml = wm * WM + 16 * i + l16;
-        if (ml >= tr.rows) continue;
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const v4f v = acc[i][j];
+          const int ml = wm * WM + 16 * i + l16;
+          *(uint2*)(smem + ml * ROW_BYTES + (wn * WN + 16 * j + 4 * q) * 2) =
+              make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
+        }
+      wait_lgkm0();                                         // the writes are in LDS
+      stage_barrier();
+      const bool n_vec = (p.N & 7) == 0;
+#pragma unroll 4
+      for (int c = tid; c < C::BM * CHUNKS; c += C::NT) {
+        const int ml = c / CHUNKS, k = c - ml * CHUNKS;
+        const int col = tr.n0 + k * 8;
+        if (ml >= tr.rows || col >= p.N) continue;
         const int row = a_row0 + ml;
         if (KIND == kContiguous) {
           const int gi = p.group_idx[row];
           const int lead = p.group_idx[(row / kAlignM) * kAlignM];
           if (gi != g || lead != g) continue;
         }
-        uint16_t* crow = p.C + (size_t)row * p.N;
+        const uint4 v = *(const uint4*)(smem + ml * ROW_BYTES + k * 16);
+        uint16_t* dst = p.C + (size_t)row * p.N + col;
+        if (n_vec && col + 8 <= p.N) {
+          *(uint4*)dst = v;
+        } else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int n = tr.n0 + wn * WN + 16 * j + 4 * q;
-          const v4f v = acc[i][j];
-          if (((p.N & 3) == 0) && n + 3 < p.N) {
-            const uint32_t lo = bf16x2_rne(v[0], v[1]);
-            const uint32_t hi = bf16x2_rne(v[2], v[3]);
-            *(uint2*)(crow + n) = make_uint2(lo, hi);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < p.N) crow[n + e] = bf16_rne(v[e]);
-          }
+          for (int e = 0; e < 8; ++e)
+            if (col + e < p.N) dst[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
         }
       }
       if (KIND != kContiguous) break;
