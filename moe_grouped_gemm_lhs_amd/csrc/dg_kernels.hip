@@ -88,6 +88,39 @@ __device__ __forceinline__ void wait_stage_copies(int wave, int ahead) {
     wait_stages_ahead<C::PER_N, A>(ahead);
 }
 
+// The tiled kernel's wait: besides `ahead` later stages of copies, `epis` tile epilogues
+// of NST stores each may have been issued after the awaited copies (vmcnt counts loads
+// and stores together, and they retire in issue order).
+template <int PER, int EXTRA, int A>
+__device__ __forceinline__ void wait_ahead_plus(int ahead) {
+  if constexpr (A <= 0) {
+    wait_vmcnt<EXTRA>();
+  } else {
+    if (ahead >= A)
+      wait_vmcnt<A * PER + EXTRA>();
+    else
+      wait_ahead_plus<PER, EXTRA, A - 1>(ahead);
+  }
+}
+template <int PER, int NST, int A, int E>
+__device__ __forceinline__ void wait_ahead_epi(int ahead, int epis) {
+  if constexpr (E <= 0) {
+    wait_ahead_plus<PER, 0, A>(ahead);
+  } else {
+    if (epis >= E)
+      wait_ahead_plus<PER, E * NST, A>(ahead);
+    else
+      wait_ahead_epi<PER, NST, A, E - 1>(ahead, epis);
+  }
+}
+template <class C, int NST>
+__device__ __forceinline__ void wait_copies_epi(int wave, int ahead, int epis) {
+  if (wave < C::S_WAVES)
+    wait_ahead_epi<C::PER_STAGE, NST, C::STAGES - 2, C::STAGES - 1>(ahead, epis);
+  else if (wave < C::CW)
+    wait_ahead_epi<C::PER_N, NST, C::STAGES - 2, C::STAGES - 1>(ahead, epis);
+}
+
 // Buffer resource over `bytes` bytes from `base` (raw, stride 0): a load at an offset
 // past the end returns zeros without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, int bytes) {
@@ -118,6 +151,14 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Read-only int32 metadata at a workgroup-uniform index, through the scalar cache (the
+// constant address space): the load counts on lgkmcnt, so waiting for it never waits for
+// the vector-memory copies and stores in flight.
+typedef const __attribute__((address_space(4))) int32_t scalar_i32;
+__device__ __forceinline__ int load_uniform(const int32_t* p, long i) {
+  return ((scalar_i32*)p)[i];
+}
 
 // Split-K partials are stored bit-inverted, so that an all-zero word marks a slot not
 // yet written.  The only value whose inverse is zero, the NaN with every bit set, is
@@ -213,6 +254,7 @@ struct TileRef {
   int row_base;  // global row (A, sA, C) of the group's row 0
   int rows;      // rows of this tile that exist (>= 1 when ok)
   int n0;
+  int lead0, lead1;  // contiguous only: group index of each 128-row block's first row
 };
 
 template <int KIND, class C>
@@ -220,6 +262,7 @@ __device__ __forceinline__ TileRef locate_tile(const GemmArgs& p, int t) {
   TileRef r;
   r.ok = 1;
   r.g2 = -1;
+  r.lead0 = r.lead1 = -1;
   int tm, tn;
   if (KIND == kMasked) {
     const int per_g = p.tiles_m * p.tiles_n;
@@ -240,7 +283,7 @@ __device__ __forceinline__ TileRef locate_tile(const GemmArgs& p, int t) {
   r.m0 = tm * C::BM;
   r.n0 = tn * C::BN;
   if (KIND == kMasked) {
-    int valid = p.masked_m[r.g];
+    int valid = load_uniform(p.masked_m, r.g);
     valid = valid < 0 ? 0 : (valid > p.rows ? p.rows : valid);
     r.row_base = r.g * p.rows;
     r.rows = min(C::BM, valid - r.m0);
@@ -251,8 +294,11 @@ __device__ __forceinline__ TileRef locate_tile(const GemmArgs& p, int t) {
     if (KIND == kContiguous) {
       // the tile holds one or two 128-row blocks; each block's leading index names
       // the only group its rows may be written with
-      r.g = p.group_idx[r.m0];
-      if (C::BM > kAlignM && r.rows > kAlignM) r.g2 = p.group_idx[r.m0 + kAlignM];
+      r.lead0 = load_uniform(p.group_idx, r.m0);
+      r.lead1 = C::BM > kAlignM && r.rows > kAlignM ? load_uniform(p.group_idx, r.m0 + kAlignM)
+                                                     : -1;
+      r.g = r.lead0;
+      r.g2 = r.lead1;
       if (r.g2 == r.g || r.g2 < 0 || r.g2 >= p.G) r.g2 = -1;
       if (r.g < 0 || r.g >= p.G) {
         r.g = r.g2;
@@ -287,7 +333,7 @@ struct TileCtx {
 // so the rows and columns past the matrix edge need no clamping and their (never
 // stored) outputs come from zeros.  Every offset is a per-lane VGPR term plus a uniform
 // term, all in the range-checked vector offset.
-template <class C>
+template <class C, bool FRESH = false>
 __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const TileCtx& c, int kb) {
   if (c.wave >= C::CW) return;             // not a copy wave
   const int sub = c.lane >> 3;             // row inside the 8-row block
@@ -297,16 +343,31 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
   const __amdgpu_buffer_rsrc_t rb =
       buffer_over(c.Bg + (size_t)c.n0 * K, min(C::BN, c.N - c.n0) * K);
   const int lane_off = sub * K + ch * 16;
+  if constexpr (FRESH) {
+    // The uniform parts are advanced copy by copy from starting values the compiler
+    // cannot see through, so it keeps no per-copy offsets or LDS addresses live from
+    // one call to the next (one per-lane term and a few scalars per call instead).
+    int ua = c.wave * (C::A_DMA * 8) * K + kb * kBlockK, da = c.wave * C::A_DMA * 1024;
+    int ub = c.wave * (C::B_DMA * 8) * K + kb * kBlockK, db = C::A_BYTES + c.wave * C::B_DMA * 1024;
+    asm volatile("" : "+s"(ua), "+s"(da), "+s"(ub), "+s"(db));
 #pragma unroll
-  for (int it = 0; it < C::A_DMA; ++it) {
-    const int cb = c.wave * C::A_DMA + it;
-    copy16<0>(ra, lane_off + (cb * 8 * K + kb * kBlockK), st + cb * 1024);
-  }
+    for (int it = 0; it < C::A_DMA; ++it, ua += 8 * K)
+      copy16<0>(ra, lane_off + ua, st + da + it * 1024);
 #pragma unroll
-  for (int it = 0; it < C::B_DMA; ++it) {
-    const int cb = c.wave * C::B_DMA + it;
-    copy16<C::B_NT ? 2 : 0>(rb, lane_off + (cb * 8 * K + kb * kBlockK),
-                            st + C::A_BYTES + cb * 1024);
+    for (int it = 0; it < C::B_DMA; ++it, ub += 8 * K)
+      copy16<C::B_NT ? 2 : 0>(rb, lane_off + ub, st + db + it * 1024);
+  } else {
+#pragma unroll
+    for (int it = 0; it < C::A_DMA; ++it) {
+      const int cb = c.wave * C::A_DMA + it;
+      copy16<0>(ra, lane_off + (cb * 8 * K + kb * kBlockK), st + cb * 1024);
+    }
+#pragma unroll
+    for (int it = 0; it < C::B_DMA; ++it) {
+      const int cb = c.wave * C::B_DMA + it;
+      copy16<C::B_NT ? 2 : 0>(rb, lane_off + (cb * 8 * K + kb * kBlockK),
+                              st + C::A_BYTES + cb * 1024);
+    }
   }
   if (c.wave < C::S_WAVES) {
     // slot s < BM: sA of row s; slot BM + j: sB of column block nb_first + j (the slots
@@ -315,7 +376,9 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
         buffer_over(c.sA + (size_t)c.a_row0 * c.nkb, c.rows * c.nkb * 4);
     const __amdgpu_buffer_rsrc_t rsb =
         buffer_over(c.sBg + (size_t)c.nb_first * c.nkb, (c.nnb - c.nb_first) * c.nkb * 4);
-    const int s_off = c.lane * c.nkb * 4 + kb * 4;
+    int sl = c.lane;
+    if (FRESH) asm volatile("" : "+v"(sl));
+    const int s_off = sl * c.nkb * 4 + kb * 4;
 #pragma unroll
     for (int it = 0; it < C::S_PER; ++it) {
       const int slot = c.wave * C::S_PER + it;
@@ -434,136 +497,307 @@ __device__ __forceinline__ void store_tile_bf16(const v4f (&acc)[C::TI][C::TJ], 
 }
 
 // ------------------------------------------------------------------------------------
-// The tiled kernel.  Each workgroup walks output tiles (persistent: blockIdx strides over
-// the tile list) and runs the whole K loop for each.
+// The tiled kernel's epilogue: a finished tile leaves through the LDS stage its last K
+// block was read from (the copies in flight fill the other stages).  In EP passes of RP
+// rows each (as many as one stage holds), the waves write their fragments of the pass's
+// rows there as bf16 rows padded by 16 bytes (the fragment writes spread over the banks),
+// then store whole rows, 16 bytes per lane, RPI rows per store instruction.
+template <class C>
+struct Epi {
+  static constexpr int ROW_BYTES = C::BN * 2 + 16;
+  static constexpr int CHUNKS = C::BN / 8;                  // 16-byte chunks per row
+  static constexpr int RPI = 64 / CHUNKS;                   // rows per store instruction
+  static constexpr int passes() {
+    int e = 1;
+    while ((C::BM / e) * ROW_BYTES > C::STAGE_BYTES) e *= 2;
+    return e;
+  }
+  static constexpr int EP = passes();
+  static constexpr int RP = C::BM / EP;
+  static constexpr int SPP = (RP + C::W * RPI - 1) / (C::W * RPI);  // stores per wave, pass
+  static constexpr int NST = EP * SPP;                      // stores per wave, tile
+  static_assert(RPI >= 1 && RP % 16 == 0 && C::BM % EP == 0, "epilogue rows");
+  static_assert((C::STAGES - 2) * C::PER_STAGE + (C::STAGES - 1) * NST < 64, "vmcnt range");
+};
+
+// Offset past every tile's output range: a buffer store there is dropped.
+constexpr int kPastTile = 0x7FFFFF00;
+
+// The finished tile an epilogue writes.
+struct TileOut {
+  int a_row0;        // global row of the tile's first row
+  int rows;          // rows that exist
+  int n0;
+  int g;             // contiguous: the group whose rows are written
+  int lead0, lead1;  // contiguous: group index of each 128-row block's first row
+};
+
+// Stores of one tile from LDS stage `st`.  Fast form (N a multiple of 8): every wave
+// issues exactly Epi::NST buffer stores, whatever the tile; a chunk outside the tile's
+// rows or columns, or in a row of another group, gets an offset past the buffer's range,
+// which the hardware drops.  Otherwise chunks are stored element by element where they
+// straddle N, and the wave waits for all of its memory operations at the end.  Returns
+// whether the fast form was used.
+template <int KIND, class C>
+__device__ __forceinline__ bool store_tile_staged(uint8_t* __restrict__ st,
+                                                  const v4f (&acc)[C::TI][C::TJ],
+                                                  const GemmArgs& p, const TileOut& o,
+                                                  int wave, int lane, int wm, int wn, int q,
+                                                  int l16) {
+  using E = Epi<C>;
+  static_assert(E::RP % C::WM == 0, "a wave's rows fall in one pass");
+  const int N = p.N;
+  const bool fast = (N & 7) == 0 && (long)C::BM * N * 2 < (long)kPastTile;
+  const __amdgpu_buffer_rsrc_t rc =
+      buffer_over(p.C + (size_t)o.a_row0 * N, fast ? o.rows * N * 2 : 0);
+  // the lane's addresses are derived here, after the tile's K loop, not hoisted out of
+  // it as loop invariants (they would hold registers through the whole loop)
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int j = ln / E::CHUNKS;                             // row inside an instruction
+  const int k = ln - j * E::CHUNKS;                         // 16-byte chunk of the row
+  const int col = o.n0 + k * 8;
+  const bool lane_ok = j < E::RPI && col < N;
+  const int e_w = uniform(C::WM * wm / E::RP);              // the pass of this wave's rows
+  // LDS byte offsets: this lane's first fragment write, and its first chunk read
+  const int wr = (C::WM * wm - e_w * E::RP + (ln & 15)) * E::ROW_BYTES + (C::WN * wn + 4 * (ln >> 4)) * 2;
+  const int rd = (wave * E::RPI + min(j, E::RPI - 1)) * E::ROW_BYTES + k * 16;
+  int out = (j * N + col) * 2;                              // + the instruction's first row
+  asm volatile("" : "+v"(out));
+  // bf16 now: the packed tile takes half the registers of the fp32 one through the passes
+  uint2 packed[C::TI][C::TJ];
+#pragma unroll
+  for (int i = 0; i < C::TI; ++i)
+#pragma unroll
+    for (int jj = 0; jj < C::TJ; ++jj)
+      packed[i][jj] = make_uint2(bf16x2_rne(acc[i][jj][0], acc[i][jj][1]),
+                                 bf16x2_rne(acc[i][jj][2], acc[i][jj][3]));
+#pragma unroll
+  for (int e = 0; e < E::EP; ++e) {
+    stage_barrier();                      // every wave is done reading the stage
+    if (e == e_w) {
+#pragma unroll
+      for (int i = 0; i < C::TI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < C::TJ; ++jj)
+          *(uint2*)(st + wr + 16 * i * E::ROW_BYTES + 32 * jj) = packed[i][jj];
+    }
+    wait_lgkm0();                         // the writes are in LDS
+    stage_barrier();
+    // which lanes store, per instruction s (its rows are the pass rows r0 .. r0+RPI-1)
+    bool ok[E::SPP];
+#pragma unroll
+    for (int s = 0; s < E::SPP; ++s) {
+      const int r0 = (s * C::W + wave) * E::RPI;
+      const int row0 = e * E::RP + r0;                      // inside the tile
+      ok[s] = lane_ok && r0 + j < E::RP && j < o.rows - row0;
+      if (KIND == kContiguous) {
+        // a row is written if it and its 128-row block's first row name the group
+        int gi = -1;
+#pragma unroll
+        for (int u = 0; u < E::RPI; ++u) {
+          const int mu = row0 + u;
+          const int lead = mu < kAlignM ? o.lead0 : o.lead1;
+          const int gu = mu < o.rows && lead == o.g ? load_uniform(p.group_idx, o.a_row0 + mu) : -1;
+          if (j == u) gi = gu;
+        }
+        ok[s] = ok[s] && gi == o.g;
+      }
+    }
+    uint4 v[E::SPP];
+#pragma unroll
+    for (int s = 0; s < E::SPP; ++s) {
+      int at = rd + s * C::W * E::RPI * E::ROW_BYTES;
+      if ((s + 1) * C::W * E::RPI > E::RP) at = min(at, (E::RP - 1) * E::ROW_BYTES + k * 16);
+      v[s] = *(const uint4*)(st + at);
+    }
+    if (fast) {
+#pragma unroll
+      for (int s = 0; s < E::SPP; ++s) {
+        const int row0 = e * E::RP + (s * C::W + wave) * E::RPI;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v[s]), rc,
+                                               ok[s] ? out + row0 * N * 2 : kPastTile, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < E::SPP; ++s) {
+        if (!ok[s]) continue;
+        const int row0 = e * E::RP + (s * C::W + wave) * E::RPI;
+        uint16_t* dst = p.C + (size_t)(o.a_row0 + row0 + j) * N + col;
+        const uint32_t w[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          if (col + x < N) dst[x] = (uint16_t)(w[x >> 1] >> ((x & 1) * 16));
+      }
+    }
+  }
+  if (!fast) wait_vmcnt<0>();
+  return fast;
+}
+
+// A workgroup's work items: tiles slot, slot + G, ... that have rows to compute; the
+// contiguous form runs a tile once per group present in it (pass 0 and 1).
+struct Work {
+  int t;
+  int pass;
+  TileRef tr;
+};
+
+template <int KIND, class C>
+__device__ __forceinline__ void next_work(const GemmArgs& p, Work& w, int G) {
+  if (KIND == kContiguous && w.pass == 0 && w.tr.g2 >= 0) {
+    w.pass = 1;
+    return;
+  }
+  w.pass = 0;
+  for (w.t += G; w.t < p.num_tiles; w.t += G) {
+    w.tr = locate_tile<KIND, C>(p, w.t);
+    if (w.tr.ok) return;
+  }
+}
+
+__device__ __forceinline__ void work_ctx(TileCtx& c, const GemmArgs& p, const Work& w) {
+  const int g = w.pass == 0 ? w.tr.g : w.tr.g2;
+  c.Bg = p.B + (size_t)g * p.N * p.K;
+  c.sBg = p.sB + (size_t)g * p.nnb * p.nkb;
+  c.a_row0 = w.tr.row_base + w.tr.m0;
+  c.rows = w.tr.rows;
+  c.n0 = w.tr.n0;
+  c.nb_first = w.tr.n0 / kBlockK;
+}
+
+// The tiled kernel's walk over a workgroup's items.  Every LDS access goes through one
+// of two restrict-qualified views of the stage buffer: `cp` for the copies, `rd` for the
+// math and the epilogue.  At any time the two touch different stages (the waits and
+// barriers order their reuse), and the restrict scopes let the compiler see that a read
+// of a stage does not depend on the copies in flight into the others.
+template <int KIND, class C>
+__device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __restrict__ rd,
+                                         const GemmArgs& p, TileCtx c, int G, int slot) {
+  constexpr int TI = C::TI, TJ = C::TJ;
+  constexpr int STAGES = C::STAGES;
+  using E = Epi<C>;
+  const int nkb = p.nkb;
+  const int nwork = p.num_tiles;
+  const int wave = c.wave;
+
+  // w: the item being multiplied; wx: the next one, whose first K blocks are copied
+  // during w's last steps (when every item has at least STAGES-1 K blocks; otherwise
+  // each item fills and drains its own pipeline)
+  Work w = {slot - G, 1, {}};
+  w.tr.g2 = -1;
+  next_work<KIND, C>(p, w, G);
+  if (w.t >= nwork) return;
+  work_ctx(c, p, w);
+  Work wx = w;
+  next_work<KIND, C>(p, wx, G);
+  TileCtx cx = c;
+  if (wx.t < nwork) work_ctx(cx, p, wx);
+  const bool cross = nkb >= STAGES - 1;
+
+  v4f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // Step kb of an item waits for its K block, starts the copy of the block STAGES-1
+  // steps later (in this item or the next) and multiplies.  `stored`: the previous
+  // item's epilogue used the fast form; its stores were issued after the copies of this
+  // item's first STAGES-1 blocks, so those steps' waits count them.
+  bool fill = true, stored = false;
+  int sn = 0, sc = 0;
+  for (;;) {
+    const bool more = cross && wx.t < nwork;
+    const int epi_n = stored ? 1 : 0;
+    if (fill) {
+      for (int f = 0; f < STAGES - 1 && f < nkb; ++f) {
+        issue_stage<C, true>(cp + sn * C::STAGE_BYTES, c, f);
+        sn = sn + 1 == STAGES ? 0 : sn + 1;
+      }
+    }
+    int kb = 0;
+    // copies of this item's later blocks
+    for (; kb + STAGES - 1 < nkb; ++kb) {
+      wait_copies_epi<C, E::NST>(wave, STAGES - 2, kb <= STAGES - 2 ? epi_n : 0);
+      stage_barrier();
+      issue_stage<C, true>(cp + sn * C::STAGE_BYTES, c, kb + STAGES - 1);
+      sn = sn + 1 == STAGES ? 0 : sn + 1;
+      compute_stage<C>(rd + sc * C::STAGE_BYTES, c, acc);
+      sc = sc + 1 == STAGES ? 0 : sc + 1;
+    }
+    // the last STAGES-1 steps: copies of the next item's first blocks, then the epilogue
+    bool fast = false;
+    for (; kb < nkb; ++kb) {
+      wait_copies_epi<C, E::NST>(wave, more ? STAGES - 2 : min(STAGES - 2, nkb - 1 - kb),
+                                 kb <= STAGES - 2 ? epi_n : 0);
+      stage_barrier();
+      if (more) {
+        issue_stage<C, true>(cp + sn * C::STAGE_BYTES, cx, kb + STAGES - 1 - nkb);
+        sn = sn + 1 == STAGES ? 0 : sn + 1;
+      }
+      compute_stage<C>(rd + sc * C::STAGE_BYTES, c, acc);
+      if (kb == nkb - 1) {
+        TileOut o;
+        o.a_row0 = c.a_row0;
+        o.rows = c.rows;
+        o.n0 = c.n0;
+        o.g = w.pass == 0 ? w.tr.g : w.tr.g2;
+        o.lead0 = w.tr.lead0;
+        o.lead1 = w.tr.lead1;
+        fast = store_tile_staged<KIND, C>(rd + sc * C::STAGE_BYTES, acc, p, o, wave, c.lane,
+                                          c.wm, c.wn, c.q, c.l16);
+      }
+      sc = sc + 1 == STAGES ? 0 : sc + 1;
+    }
+    if (wx.t >= nwork) break;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    stored = fast && cross;
+    fill = !cross;
+    w = wx;
+    c = cx;
+    next_work<KIND, C>(p, wx, G);
+    if (wx.t < nwork) work_ctx(cx, p, wx);
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// The tiled kernel.  Each workgroup walks its work items (persistent: blockIdx strides
+// over the tile list) with one copy pipeline through all of them: the copies of the next
+// item's first K blocks are in flight while the current item finishes and stores its
+// tile, and the epilogue's stores are counted in the waits instead of being drained.
 template <int KIND, class C>
 __global__ void __launch_bounds__(C::NT)
 gemm_fp8_kernel(GemmArgs p) {
-  constexpr int WM = C::WM, WN = C::WN, TI = C::TI, TJ = C::TJ;
-  constexpr int STAGES = C::STAGES;
   // The kernel's only LDS variable: a second one would make the compiler tag LDS
   // accesses with per-variable alias scopes, dropping the restrict scopes that keep it
-  // from waiting on in-flight stage copies (see kb_step).
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * C::STAGE_BYTES];
+  // from waiting on in-flight stage copies.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::STAGES * C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
-  const int wm = wave / C::WAVES_N;
-  const int wn = wave - wm * C::WAVES_N;
-  const int q = lane >> 4;
-  const int l16 = lane & 15;
-  const int K = p.K;
-  const int nkb = p.nkb;
+  TileCtx c;
+  c.A = p.A;
+  c.sA = p.sA;
+  c.K = p.K;
+  c.nkb = p.nkb;
+  c.nnb = p.nnb;
+  c.N = p.N;
+  c.lane = tid & 63;
+  c.wave = uniform(tid >> 6);
+  c.wm = c.wave / C::WAVES_N;
+  c.wn = c.wave - c.wm * C::WAVES_N;
+  c.q = c.lane >> 4;
+  c.l16 = c.lane & 15;
 
   // XCD-aware order: workgroups are dispatched round-robin over the 8 XCDs, so give
   // each XCD a contiguous run of work items (neighbouring tiles share its L2).
-  const int nwork = p.num_tiles;
   const int G = gridDim.x;
   const int xcd_runs = (G % 8 == 0) ? 8 : 1;
   const int slot = (blockIdx.x % xcd_runs) * (G / xcd_runs) + blockIdx.x / xcd_runs;
-
-  for (int t = slot; t < nwork; t += G) {
-    const TileRef tr = locate_tile<KIND, C>(p, t);
-    if (!tr.ok) continue;
-    const int kb_begin = 0;
-    const int nk = nkb;
-    const int a_row0 = tr.row_base + tr.m0;
-
-    // contiguous layout: up to two passes (one per group present in the tile)
-    for (int pass = 0; pass < 2; ++pass) {
-      const int g = pass == 0 ? tr.g : tr.g2;
-      if (g < 0) break;
-      TileCtx c;
-      c.A = p.A;
-      c.sA = p.sA;
-      c.Bg = p.B + (size_t)g * p.N * K;
-      c.sBg = p.sB + (size_t)g * p.nnb * nkb;
-      c.K = K;
-      c.nkb = nkb;
-      c.nnb = p.nnb;
-      c.N = p.N;
-      c.a_row0 = a_row0;
-      c.rows = tr.rows;
-      c.n0 = tr.n0;
-      c.nb_first = tr.n0 / kBlockK;
-      c.wave = wave;
-      c.lane = lane;
-      c.wm = wm;
-      c.wn = wn;
-      c.q = q;
-      c.l16 = l16;
-
-      wait_vmcnt<0>();   // earlier stores must not be counted as staging loads
-      __syncthreads();   // every wave is done reading the stages of the previous tile
-
-      v4f acc[TI][TJ];
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-      // iterations 1-STAGES .. -1 only fill the pipeline (STAGES-1 blocks in flight);
-      // iteration it >= 0 waits for block `it`, starts block it+STAGES-1, multiplies `it`
-      for (int it = 1 - STAGES; it < nk; ++it) {
-        if (it >= 0) {
-          // block `it` has landed once only the blocks issued after it are in flight
-          wait_stage_copies<C, STAGES - 2>(wave, min(STAGES - 2, nk - 1 - it));
-          stage_barrier();
-        }
-        const int nxt = it + STAGES - 1;
-        const int cur = it < 0 ? 0 : it;
-        kb_step<C>(smem + (nxt % STAGES) * C::STAGE_BYTES, smem + (cur % STAGES) * C::STAGE_BYTES, c,
-                   nxt < nk, kb_begin + nxt, c, it >= 0, acc);
-      }
-
-      // ---------------------------------------------------------------- epilogue
-      // The tile goes out through LDS, free once every wave is past the last stage: the
-      // waves write their fragments there as bf16 rows, then the workgroup stores whole
-      // row segments, 16 bytes per lane with consecutive lanes along a row (straight
-      // from the MFMA layout a store instruction would cover 16 rows x 32 bytes).  Rows
-      // are padded by 16 bytes so that the fragment writes spread over the banks.
-      constexpr int ROW_BYTES = C::BN * 2 + 16;
-      constexpr int CHUNKS = C::BN / 8;                    // 16-byte chunks per row
-      static_assert(C::BM * ROW_BYTES <= STAGES * C::STAGE_BYTES, "epilogue staging");
-      stage_barrier();                                      // the stages are free
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const v4f v = acc[i][j];
-          const int ml = wm * WM + 16 * i + l16;
-          *(uint2*)(smem + ml * ROW_BYTES + (wn * WN + 16 * j + 4 * q) * 2) =
-              make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
-        }
-      wait_lgkm0();                                         // the writes are in LDS
-      stage_barrier();
-      const bool n_vec = (p.N & 7) == 0;
-#pragma unroll 4
-      for (int c = tid; c < C::BM * CHUNKS; c += C::NT) {
-        const int ml = c / CHUNKS, k = c - ml * CHUNKS;
-        const int col = tr.n0 + k * 8;
-        if (ml >= tr.rows || col >= p.N) continue;
-        const int row = a_row0 + ml;
-        if (KIND == kContiguous) {
-          const int gi = p.group_idx[row];
-          const int lead = p.group_idx[(row / kAlignM) * kAlignM];
-          if (gi != g || lead != g) continue;
-        }
-        const uint4 v = *(const uint4*)(smem + ml * ROW_BYTES + k * 16);
-        uint16_t* dst = p.C + (size_t)row * p.N + col;
-        if (n_vec && col + 8 <= p.N) {
-          *(uint4*)dst = v;
-        } else {
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (col + e < p.N) dst[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
-        }
-      }
-      if (KIND != kContiguous) break;
-    }
-  }
+  tile_walk<KIND, C>(smem, smem, p, c, G, slot);
 }
 
 // ------------------------------------------------------------------------------------
