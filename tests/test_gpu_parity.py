@@ -95,6 +95,48 @@ def test_every_instance_on_ragged_problem(kind, monkeypatch):
     monkeypatch.delenv("DG_FORCE_INSTANCE")
 
 
+# tiled instances and problems with more tiles than workgroups (several work items per
+# workgroup, so the copy pipeline crosses item boundaries); K = 128 / 256 gives items
+# shorter than the 3- and 4-stage pipelines (each item then fills and drains its own)
+TILED_CASES = [
+    # (instance, kind, rows or group sizes / (G, cap), tile columns, K values)
+    ("dense_256x256", "dense", 4096, 17 * 256, (128, 384)),
+    ("dense_256x224", "dense", 4096, 17 * 224, (128, 384)),
+    ("dense_256x160", "dense", 4096, 17 * 160, (256,)),
+    ("dense_128x128", "dense", 2048, 17 * 128, (128, 256)),
+    ("contig_256x256", "contiguous", [1152, 896, 2048], 17 * 256, (128, 384)),
+    ("contig_256x224", "contiguous", [1152, 896, 2048], 17 * 224, (256,)),
+    ("contig_128x128", "contiguous", [640, 384, 1024], 17 * 128, (128, 256)),
+    ("masked_256x256", "masked", (2, 2048), 17 * 256, (128,)),
+    ("masked_128x128", "masked", (2, 1024), 17 * 128, (128, 256)),
+    ("masked_64x128", "masked", (4, 512), 9 * 128, (128, 256, 384)),
+]
+
+
+@pytest.mark.parametrize("case", TILED_CASES, ids=[c[0] for c in TILED_CASES])
+@pytest.mark.parametrize("ragged_n", [False, True], ids=["n8", "nodd"])
+def test_tiled_pipeline_across_items(case, ragged_n, monkeypatch):
+    """Each tiled instance on a problem with more tiles than the persistent grid, for
+    short and longer K, with N a multiple of 8 (fixed-count stores) and not (element-wise
+    stores at the right edge); every row checked for routing, sampled rows against the
+    oracle."""
+    name, kind, rows, n, ks = case
+    n = n - 3 if ragged_n else n
+    monkeypatch.setenv("DG_FORCE_INSTANCE", name)
+    for K in ks:
+        seed = len(name) + K // 128 + (1 if ragged_n else 0)
+        if kind == "dense":
+            p = I.make_dense(rows, n, K, seed=seed)
+        elif kind == "contiguous":
+            p = I.make_contiguous(rows, n, K, seed=seed)
+        else:
+            G, cap = rows
+            p = I.make_masked(G, cap, n, K, seed=seed,
+                              masked_m=[cap - 1 - 300 * g for g in range(G)])
+        check_sampled(p, f"{name} N={n} K={K} across items", seed=K)
+    monkeypatch.delenv("DG_FORCE_INSTANCE")
+
+
 STREAM_INSTANCES = ["dense_64x64_stream", "dense_64x128_stream", "dense_128x64_stream",
                     "dense_128x128_stream"]
 
