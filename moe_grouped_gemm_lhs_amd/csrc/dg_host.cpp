@@ -364,7 +364,7 @@ static dg_status quantize(int block128x128, const void* X, int x_dtype, uint8_t*
   const dg_status st = check_device(&num_cus);
   if (st != DG_OK) return st;
   (void)hipGetLastError();
-  dg::launch_quantize(block128x128, format, x_dtype == DG_IN_BF16, X, Q, S, rows, K,
+  dg::launch_quantize(block128x128, format, x_dtype == DG_IN_BF16, X, Q, S, rows, K, num_cus,
                       (hipStream_t)stream);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }

@@ -81,7 +81,7 @@ const Instance* instances(int* count);
 
 // fp8 block quantisation launch (defined in dg_quant.hip); arguments already validated.
 void launch_quantize(int block128x128, int fmt, int bf16, const void* X, uint8_t* Q, float* S,
-                     int64_t rows, int64_t K, hipStream_t stream);
+                     int64_t rows, int64_t K, int num_cus, hipStream_t stream);
 
 // Byte-matrix transposition (defined in dg_quant.hip); arguments already validated.
 void launch_transpose_u8(const uint8_t* X, uint8_t* Y, int64_t rows, int64_t cols,

@@ -332,7 +332,9 @@ struct TileCtx {
 // scales): a lane whose offset falls past the end reads zeros without touching memory,
 // so the rows and columns past the matrix edge need no clamping and their (never
 // stored) outputs come from zeros.  Every offset is a per-lane VGPR term plus a uniform
-// term, all in the range-checked vector offset.
+// term, all in the range-checked vector offset.  FRESH (the tiled kernel, whose loops
+// keep more state live): the offsets are rebuilt at every call instead of kept in
+// registers across calls.
 template <class C, bool FRESH = false>
 __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const TileCtx& c, int kb) {
   if (c.wave >= C::CW) return;             // not a copy wave

@@ -28,9 +28,14 @@ struct In {
   static constexpr int E = BF16 ? 8 : 4;
 };
 
+// The 16-byte load behind E inputs, and its expansion to fp32.
 template <bool BF16>
-__device__ __forceinline__ void load16(const void* X, int64_t i, float (&x)[In<BF16>::E]) {
-  const uint4 u = *(const uint4*)((const uint8_t*)X + i * (BF16 ? 2 : 4));
+__device__ __forceinline__ uint4 load_raw(const void* X, int64_t i) {
+  return *(const uint4*)((const uint8_t*)X + i * (BF16 ? 2 : 4));
+}
+
+template <bool BF16>
+__device__ __forceinline__ void expand(const uint4& u, float (&x)[In<BF16>::E]) {
   if (BF16) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -114,7 +119,7 @@ quant_1x128_kernel(const void* X, uint8_t* Q, float* S, int64_t nblk, int nkb, i
     const int64_t bb = b[u] < nblk ? b[u] : nblk - 1;
     const int64_t r = bb / nkb;
     i[u] = r * K + (bb - r * nkb) * kBlockK + l * E;
-    load16<BF16>(X, i[u], x[u]);
+    expand<BF16>(load_raw<BF16>(X, i[u]), x[u]);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -131,50 +136,83 @@ quant_1x128_kernel(const void* X, uint8_t* Q, float* S, int64_t nblk, int nkb, i
   }
 }
 
-// 128x128 blocks: one 256-thread workgroup per block; thread t takes the E columns
-// starting at E(t % (128/E)) of rows t / (128/E) + R j, j = 0 .. 128/R - 1, where
-// R = 256 / (128/E) rows are covered per pass (rows past the matrix are skipped).
+// 128x128 blocks: a persistent grid of a few workgroups per CU strides over the blocks,
+// each workgroup loading its next block while it quantises the current one, so that
+// every CU gets the same number of blocks (no partly filled last wave of workgroups) and
+// the loads of consecutive blocks overlap.  Thread t takes the E columns starting at
+// E(t % (128/E)) of rows t / (128/E) + R j, j = 0 .. 128/R - 1, where R = 256 / (128/E)
+// rows are covered per pass (rows past the matrix read as zero and are not stored).  The
+// block maximum goes through LDS, double buffered so that one barrier per block suffices.
 template <int FMT, bool BF16>
 __global__ void __launch_bounds__(256)
-quant_128x128_kernel(const void* X, uint8_t* Q, float* S, int64_t rows, int nkb, int64_t K) {
+quant_128x128_kernel(const void* X, uint8_t* Q, float* S, int64_t rows, int nkb, int64_t K,
+                     int64_t nblk) {
   constexpr int E = In<BF16>::E, TPR = kBlockK / E, R = 256 / TPR, J = kBlockK / R;
-  __shared__ float wave_max[4];
-  const int64_t b = blockIdx.x;
-  const int64_t rb = b / nkb;
-  const int kb = (int)(b - rb * nkb);
+  __shared__ float wave_max[2][4];
   const int t = threadIdx.x;
-  const int64_t col = (int64_t)kb * kBlockK + (t % TPR) * E;
-  const int64_t row0 = rb * kBlockK + t / TPR;
-  float x[J][E];
-  float amax = 0.0f;
+  const int64_t G = gridDim.x;
+  const int lr = t / TPR;                                  // row inside a pass
+  const int lc = (t % TPR) * E;                            // column inside the block
+  auto load_block = [&](int64_t b, uint4 (&raw)[J]) {
+    const int64_t rb = b / nkb;
+    const int64_t col = (b - rb * nkb) * kBlockK + lc, row0 = rb * kBlockK + lr;
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int64_t r = row0 + R * j;
-    if (r < rows) {
-      load16<BF16>(X, r * K + col, x[j]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) x[j][e] = 0.0f;
+    for (int j = 0; j < J; ++j) {
+      const int64_t r = row0 + R * j;
+      raw[j] = r < rows ? load_raw<BF16>(X, r * K + col) : make_uint4(0, 0, 0, 0);
     }
-    amax = fmaxf(amax, amax_of<E>(x[j]));
-  }
+  };
+  int64_t b = blockIdx.x;
+  uint4 cur[J];
+  load_block(b, cur);
+  for (int k = 0; b < nblk; ++k, b += G) {
+    uint4 nxt[J];
+    const bool more = b + G < nblk;
+    if (more) load_block(b + G, nxt);
+    float amax = 0.0f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  if ((t & 63) == 0) wave_max[t >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
-  const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<FMT>();
-  const float rcp = 1.0f / scale;                          // correctly rounded
-  if (t == 0) S[b] = scale;
+    for (int j = 0; j < J; ++j) {
+      float x[E];
+      expand<BF16>(cur[j], x);
+      amax = fmaxf(amax, amax_of<E>(x));
+    }
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int64_t r = row0 + R * j;
-    if (r < rows) store_codes<FMT, BF16>(Q, r * K + col, x[j], scale, rcp);
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if ((t & 63) == 0) wave_max[k & 1][t >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wave_max[k & 1][0], wave_max[k & 1][1]),
+                 fmaxf(wave_max[k & 1][2], wave_max[k & 1][3]));
+    const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<FMT>();
+    const float rcp = 1.0f / scale;                        // correctly rounded
+    if (t == 0) S[b] = scale;
+    const int64_t rb = b / nkb;
+    const int64_t col = (b - rb * nkb) * kBlockK + lc, row0 = rb * kBlockK + lr;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int64_t r = row0 + R * j;
+      if (r < rows) {
+        float x[E];
+        expand<BF16>(cur[j], x);
+        store_codes<FMT, BF16>(Q, r * K + col, x, scale, rcp);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) cur[j] = nxt[j];
+    }
   }
 }
 
+// Persistent grid: `per_cu` workgroups per CU at most, each taking the same number of
+// blocks (the grid shrinks so that the blocks divide as evenly as they can).
+int64_t persistent_grid(int64_t pieces, int num_cus, int per_cu) {
+  const int64_t slots = (int64_t)num_cus * per_cu;
+  const int64_t each = (pieces + slots - 1) / slots;
+  return (pieces + each - 1) / each;
+}
+
 template <int FMT, bool BF16>
-void launch_1x128(const void* X, uint8_t* Q, float* S, int64_t rows, int64_t K,
+void launch_1x128(const void* X, uint8_t* Q, float* S, int64_t rows, int64_t K, int,
                   hipStream_t stream) {
   constexpr int E = In<BF16>::E, BPW = 64 / (kBlockK / E), U = 4;
   const int nkb = (int)(K / kBlockK);
@@ -185,12 +223,14 @@ void launch_1x128(const void* X, uint8_t* Q, float* S, int64_t rows, int64_t K,
 }
 
 template <int FMT, bool BF16>
-void launch_128x128(const void* X, uint8_t* Q, float* S, int64_t rows, int64_t K,
+void launch_128x128(const void* X, uint8_t* Q, float* S, int64_t rows, int64_t K, int num_cus,
                     hipStream_t stream) {
   const int nkb = (int)(K / kBlockK);
   const int64_t nblk = ((rows + kBlockK - 1) / kBlockK) * nkb;
-  hipLaunchKernelGGL((quant_128x128_kernel<FMT, BF16>), dim3((unsigned)nblk), dim3(256), 0,
-                     stream, X, Q, S, rows, nkb, K);
+  // as many workgroups per CU as the registers admit (two blocks' loads per thread)
+  const int64_t grid = persistent_grid(nblk, num_cus, BF16 ? 4 : 3);
+  hipLaunchKernelGGL((quant_128x128_kernel<FMT, BF16>), dim3((unsigned)grid), dim3(256), 0,
+                     stream, X, Q, S, rows, nkb, K, nblk);
 }
 
 }  // namespace
@@ -198,21 +238,21 @@ void launch_128x128(const void* X, uint8_t* Q, float* S, int64_t rows, int64_t K
 // Host-side dispatch over (block shape, format, input type); the caller has validated
 // every argument.
 void launch_quantize(int block128x128, int fmt, int bf16, const void* X, uint8_t* Q, float* S,
-                     int64_t rows, int64_t K, hipStream_t stream) {
+                     int64_t rows, int64_t K, int num_cus, hipStream_t stream) {
   if (block128x128) {
     if (fmt == kFmtE5M2)
-      bf16 ? launch_128x128<kFmtE5M2, true>(X, Q, S, rows, K, stream)
-           : launch_128x128<kFmtE5M2, false>(X, Q, S, rows, K, stream);
+      bf16 ? launch_128x128<kFmtE5M2, true>(X, Q, S, rows, K, num_cus, stream)
+           : launch_128x128<kFmtE5M2, false>(X, Q, S, rows, K, num_cus, stream);
     else
-      bf16 ? launch_128x128<kFmtE4M3, true>(X, Q, S, rows, K, stream)
-           : launch_128x128<kFmtE4M3, false>(X, Q, S, rows, K, stream);
+      bf16 ? launch_128x128<kFmtE4M3, true>(X, Q, S, rows, K, num_cus, stream)
+           : launch_128x128<kFmtE4M3, false>(X, Q, S, rows, K, num_cus, stream);
   } else {
     if (fmt == kFmtE5M2)
-      bf16 ? launch_1x128<kFmtE5M2, true>(X, Q, S, rows, K, stream)
-           : launch_1x128<kFmtE5M2, false>(X, Q, S, rows, K, stream);
+      bf16 ? launch_1x128<kFmtE5M2, true>(X, Q, S, rows, K, num_cus, stream)
+           : launch_1x128<kFmtE5M2, false>(X, Q, S, rows, K, num_cus, stream);
     else
-      bf16 ? launch_1x128<kFmtE4M3, true>(X, Q, S, rows, K, stream)
-           : launch_1x128<kFmtE4M3, false>(X, Q, S, rows, K, stream);
+      bf16 ? launch_1x128<kFmtE4M3, true>(X, Q, S, rows, K, num_cus, stream)
+           : launch_1x128<kFmtE4M3, false>(X, Q, S, rows, K, num_cus, stream);
   }
 }
 

@@ -59,6 +59,16 @@ def test_quantize_bit_exact(kind, shapes, fmt, dtype):
         check(x, fmt, kind, getattr(torch, dtype), f"{rows}x{K}")
 
 
+@pytest.mark.parametrize("kind,rows,K", [("1x128", 600, 16384), ("128x128", 1100, 16384)])
+@pytest.mark.parametrize("fmt,dtype", [("e4m3", "bfloat16"), ("e5m2", "float32")])
+def test_quantize_large_shapes(kind, rows, K, fmt, dtype):
+    """Larger shapes: for 128x128 blocks more blocks than the persistent grid has
+    workgroups, so each workgroup loads its next block while it quantises the current
+    one (with a ragged row count)."""
+    x = I.normal_matrix(90 + rows, 1, rows, K, outliers=True)
+    check(x, fmt, kind, getattr(torch, dtype), f"{rows}x{K} several pieces")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("kind", ["1x128", "128x128"])
 def test_quantize_ties_zeros_saturation(fmt, kind):
