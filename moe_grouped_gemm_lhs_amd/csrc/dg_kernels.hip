@@ -637,6 +637,83 @@ __device__ __forceinline__ bool store_tile_staged(uint8_t* __restrict__ st,
   return fast;
 }
 
+// The direct epilogue (dense and masked forms): no LDS and no barrier.  Lane (l16, q) of
+// a wave holds columns 4q .. 4q+3 of row l16 of every 16x16 fragment.  For fragments j
+// and j+1, one v_permlane16_swap per packed bf16 word exchanges the odd 16-lane groups of
+// fragment j with the even ones of fragment j+1, after which lane (l16, q) holds the 8
+// consecutive columns 16(j + (q & 1)) + 8(q >> 1) .. +7 of its row: one 16-byte store, a
+// store instruction covering 16 rows x 64 bytes.  An odd last fragment is stored 8 bytes
+// per lane.  Fast form (N a multiple of 8): a fixed count of buffer stores per wave
+// (Epi::direct_stores), chunks outside the tile's rows or columns dropped by an offset
+// past the buffer's range; otherwise element-wise stores and a full wait at the end.
+template <class C>
+constexpr int direct_stores() {
+  return C::TI * ((C::TJ + 1) / 2);
+}
+
+template <class C>
+__device__ __forceinline__ bool store_tile_direct(const v4f (&acc)[C::TI][C::TJ],
+                                                  const GemmArgs& p, const TileOut& o, int wm,
+                                                  int wn, int lane) {
+  const int N = p.N;
+  const bool fast = (N & 7) == 0 && (long)C::BM * N * 2 < (long)kPastTile;
+  int ln = lane;
+  asm volatile("" : "+v"(ln));           // lane terms computed here, not kept live
+  const int l16 = ln & 15, q = ln >> 4;
+  const int row_w = C::WM * wm + l16;    // this lane's row in the tile, first fragment row
+  const int col_w = o.n0 + C::WN * wn;   // the wave's first column
+  if (fast) {
+    const __amdgpu_buffer_rsrc_t rc = buffer_over(p.C + (size_t)o.a_row0 * N, o.rows * N * 2);
+    const int col_pair = col_w + 16 * (q & 1) + 8 * (q >> 1);   // + 16 j for pair (j, j+1)
+    const int col_one = col_w + 4 * q;                         // + 16 j, odd last fragment
+#pragma unroll
+    for (int i = 0; i < C::TI; ++i) {
+      const int r = row_w + 16 * i;
+      const bool row_ok = r < o.rows;
+      const int row_off = r * N;
+#pragma unroll
+      for (int j = 0; j + 1 < C::TJ; j += 2) {
+        const v4f a = acc[i][j], b = acc[i][j + 1];
+        const uint32_t a0 = bf16x2_rne(a[0], a[1]), a1 = bf16x2_rne(a[2], a[3]);
+        const uint32_t b0 = bf16x2_rne(b[0], b[1]), b1 = bf16x2_rne(b[2], b[3]);
+        const auto s0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+        const v4i v = {(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+        const int col = col_pair + 16 * j;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc,
+                                               row_ok && col < N ? (row_off + col) * 2 : kPastTile,
+                                               0, 0);
+      }
+      if constexpr (C::TJ % 2 == 1) {
+        const v4f a = acc[i][C::TJ - 1];
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = {bf16x2_rne(a[0], a[1]), bf16x2_rne(a[2], a[3])};
+        const int col = col_one + 16 * (C::TJ - 1);
+        __builtin_amdgcn_raw_buffer_store_b64(v, rc,
+                                              row_ok && col < N ? (row_off + col) * 2 : kPastTile,
+                                              0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::TI; ++i) {
+      const int r = row_w + 16 * i;
+      if (r >= o.rows) continue;
+      uint16_t* crow = p.C + (size_t)(o.a_row0 + r) * N;
+#pragma unroll
+      for (int j = 0; j < C::TJ; ++j) {
+        const int n = col_w + 16 * j + 4 * q;
+        const v4f v = acc[i][j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < N) crow[n + e] = bf16_rne(v[e]);
+      }
+    }
+    wait_vmcnt<0>();
+  }
+  return fast;
+}
+
 // A workgroup's work items: tiles slot, slot + G, ... that have rows to compute; the
 // contiguous form runs a tile once per group present in it (pass 0 and 1).
 struct Work {
@@ -679,6 +756,11 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
   constexpr int TI = C::TI, TJ = C::TJ;
   constexpr int STAGES = C::STAGES;
   using E = Epi<C>;
+  // the contiguous form goes through LDS (its row checks read group indices per row);
+  // the others store from registers
+  constexpr bool DIRECT = KIND != kContiguous;
+  constexpr int NST = DIRECT ? direct_stores<C>() : E::NST;
+  static_assert((STAGES - 2) * C::PER_STAGE + (STAGES - 1) * NST < 64, "vmcnt range");
   const int nkb = p.nkb;
   const int nwork = p.num_tiles;
   const int wave = c.wave;
@@ -721,7 +803,7 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
     int kb = 0;
     // copies of this item's later blocks
     for (; kb + STAGES - 1 < nkb; ++kb) {
-      wait_copies_epi<C, E::NST>(wave, STAGES - 2, kb <= STAGES - 2 ? epi_n : 0);
+      wait_copies_epi<C, NST>(wave, STAGES - 2, kb <= STAGES - 2 ? epi_n : 0);
       stage_barrier();
       issue_stage<C, true>(cp + sn * C::STAGE_BYTES, c, kb + STAGES - 1);
       sn = sn + 1 == STAGES ? 0 : sn + 1;
@@ -731,7 +813,7 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
     // the last STAGES-1 steps: copies of the next item's first blocks, then the epilogue
     bool fast = false;
     for (; kb < nkb; ++kb) {
-      wait_copies_epi<C, E::NST>(wave, more ? STAGES - 2 : min(STAGES - 2, nkb - 1 - kb),
+      wait_copies_epi<C, NST>(wave, more ? STAGES - 2 : min(STAGES - 2, nkb - 1 - kb),
                                  kb <= STAGES - 2 ? epi_n : 0);
       stage_barrier();
       if (more) {
@@ -747,8 +829,11 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
         o.g = w.pass == 0 ? w.tr.g : w.tr.g2;
         o.lead0 = w.tr.lead0;
         o.lead1 = w.tr.lead1;
-        fast = store_tile_staged<KIND, C>(rd + sc * C::STAGE_BYTES, acc, p, o, wave, c.lane,
-                                          c.wm, c.wn, c.q, c.l16);
+        if constexpr (DIRECT)
+          fast = store_tile_direct<C>(acc, p, o, c.wm, c.wn, c.lane);
+        else
+          fast = store_tile_staged<KIND, C>(rd + sc * C::STAGE_BYTES, acc, p, o, wave, c.lane,
+                                            c.wm, c.wn, c.q, c.l16);
       }
       sc = sc + 1 == STAGES ? 0 : sc + 1;
     }
