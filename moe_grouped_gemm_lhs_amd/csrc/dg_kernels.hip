@@ -499,8 +499,9 @@ __device__ __forceinline__ void store_tile_bf16(const v4f (&acc)[C::TI][C::TJ], 
 }
 
 // ------------------------------------------------------------------------------------
-// The tiled kernel's epilogue: a finished tile leaves through the LDS stage its last K
-// block was read from (the copies in flight fill the other stages).  In EP passes of RP
+// The tiled kernel's LDS-staged epilogue (the contiguous form, whose row checks read the
+// group indices of whole rows; the other forms store from registers, below): a finished
+// tile leaves through the LDS stage its last K block was read from (the copies in flight fill the other stages).  In EP passes of RP
 // rows each (as many as one stage holds), the waves write their fragments of the pass's
 // rows there as bf16 rows padded by 16 bytes (the fragment writes spread over the banks),
 // then store whole rows, 16 bytes per lane, RPI rows per store instruction.
