@@ -67,12 +67,16 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Shape rules shared by every call.  rows_or_cap = M, M_total or cap.
+constexpr int64_t kMaxK = (int64_t)1 << 22;
+
 dg_status check_shape(int kind, int64_t rows_or_cap, int64_t N, int64_t K, int64_t G) {
   if (K <= 0 || K % dg::kBlockK != 0) return DG_ERR_SHAPE;
   if (rows_or_cap < 0 || N < 0 || G < 1) return DG_ERR_SHAPE;
   // 32-bit row, column and tile indices inside the kernels
   if (G > INT32_MAX || rows_or_cap > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
     return DG_ERR_SHAPE;
+  // 32-bit byte offsets inside a tile's rows of A and B (up to 256 rows of K bytes)
+  if (K > kMaxK) return DG_ERR_SHAPE;
   if (kind == dg::kMasked && rows_or_cap * G > INT32_MAX) return DG_ERR_SHAPE;
   return DG_OK;
 }
