@@ -35,7 +35,7 @@
  *     Column n of C uses row n/128 of its group's sB; N need not be a multiple of 128.
  *   - Preconditions checked on the host, before any device work, in this order:
  *       shapes: 0 < K <= 2^22 and K % 128 == 0, M/N >= 0, G >= 1,
- *       cap >= 0                                                  -> DG_ERR_SHAPE
+ *       cap >= 0, fewer than 2^31 64x64 output tiles              -> DG_ERR_SHAPE
  *       operand formats (the _ex calls) DG_FP8_E4M3 or DG_FP8_E5M2  -> DG_ERR_FORMAT
  *       an empty output (no rows or N == 0) returns DG_OK without touching anything
  *       pointers non-NULL                                         -> DG_ERR_NULL

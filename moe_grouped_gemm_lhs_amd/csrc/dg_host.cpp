@@ -77,6 +77,9 @@ dg_status check_shape(int kind, int64_t rows_or_cap, int64_t N, int64_t K, int64
     return DG_ERR_SHAPE;
   // 32-bit byte offsets inside a tile's rows of A and B (up to 256 rows of K bytes)
   if (K > kMaxK) return DG_ERR_SHAPE;
+  // 32-bit tile indices, counted for the smallest tile (64 x 64)
+  const int64_t groups = kind == dg::kMasked ? G : 1;
+  if ((rows_or_cap + 63) / 64 * ((N + 63) / 64) > INT32_MAX / groups) return DG_ERR_SHAPE;
   if (kind == dg::kMasked && rows_or_cap * G > INT32_MAX) return DG_ERR_SHAPE;
   return DG_OK;
 }
@@ -184,13 +187,16 @@ const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_
   return name ? find_instance(name, fa, fb) : nullptr;
 }
 
-void fill_tiles(GemmArgs& a, const Instance* in, int kind) {
+// false if the tile count does not fit the kernels' 32-bit tile indices
+bool fill_tiles(GemmArgs& a, const Instance* in, int kind) {
   a.nkb = a.K / dg::kBlockK;
   a.nnb = (int)cdiv(a.N, dg::kBlockK);
   a.tiles_m = (int)cdiv(a.rows, in->bm);
   a.tiles_n = (int)cdiv(a.N, in->bn);
-  a.num_tiles = a.tiles_m * a.tiles_n * (kind == dg::kMasked ? a.G : 1);
+  const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n * (kind == dg::kMasked ? a.G : 1);
+  a.num_tiles = tiles > INT32_MAX ? 0 : (int)tiles;
   a.band = a.tiles_m < 4 ? a.tiles_m : 4;
+  return tiles <= INT32_MAX;
 }
 
 size_t workspace_for(const Instance* in, const GemmArgs& a) {
@@ -204,7 +210,7 @@ dg_status run(int kind, int fa, int fb, GemmArgs& a, void* workspace, size_t wor
               void* stream) {
   const Instance* in = select_instance(kind, a.rows, a.N, a.K, a.G, fa, fb);
   if (!in) return DG_ERR_SHAPE;
-  fill_tiles(a, in, kind);
+  if (!fill_tiles(a, in, kind)) return DG_ERR_SHAPE;
   const size_t ws = workspace_for(in, a);
   if (ws > 0) {
     if (!workspace || workspace_bytes < ws || !aligned(workspace, 16)) return DG_ERR_WORKSPACE;
@@ -258,7 +264,7 @@ size_t dg_workspace_bytes(int kind, int64_t rows_or_cap, int64_t N, int64_t K, i
   a.N = (int)N;
   a.K = (int)K;
   a.G = (int)G;
-  fill_tiles(a, in, kind);
+  if (!fill_tiles(a, in, kind)) return 0;
   return workspace_for(in, a);
 }
 

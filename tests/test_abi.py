@@ -68,6 +68,7 @@ def test_dense_validation_codes(lib):
     assert dense(lib, sA=A4 + 1) == 3
     assert dense(lib, M=1 << 31) == 2
     assert dense(lib, K=1 << 23) == 2     # 32-bit offsets within a tile's rows of A and B
+    assert dense(lib, M=1 << 30, N=1 << 30) == 2   # more tiles than 32-bit tile indices
 
 
 def test_format_validation_codes(lib):
