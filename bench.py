@@ -423,7 +423,7 @@ _ROOT = os.path.dirname(os.path.abspath(__file__))
 _KERNEL_SOURCES = ["moe_grouped_gemm_lhs_amd/csrc/dg_kernels.hip",
                    "moe_grouped_gemm_lhs_amd/csrc/dg_internal.h",
                    "moe_grouped_gemm_lhs_amd/csrc/dg_host.cpp"]
-_TRAFFIC_FILES = {("dense_128x128_stream", "dense_128x7168x16384"):
+_TRAFFIC_FILES = {("dense_128x128_stream_4w", "dense_128x7168x16384"):
                   "profiles/decode_stream_kernel_hbm_traffic.txt"}
 
 

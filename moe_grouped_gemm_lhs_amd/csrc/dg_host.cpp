@@ -137,12 +137,17 @@ const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_
         // tiles; measured: 64x24576x1536 17.5 -> 12.1 us and 128x4096x7168 18.9 -> 17.4
         // us with 128 columns; 2112x7168 and 7168x2048 keep 64)
         const int64_t tiles128 = cdiv(N, 128), nkb = K / dg::kBlockK;
-        const bool wide =
-            4 * dg::stream_grid(tiles128, nkb, kAssumedCUs) >= 3 * kAssumedCUs;
+        const int64_t grid128 = dg::stream_grid(tiles128, nkb, kAssumedCUs);
+        const bool wide = 4 * grid128 >= 3 * kAssumedCUs;
+        // ranges of 16 K blocks or more per workgroup: the 4-wave build of the 128-column
+        // tile (128x7168x16384: 44.0 -> 39.7 us; it loses 2-7% on shorter ranges)
+        const bool long_range = tiles128 * nkb >= 16 * grid128;
         if (rows_or_cap <= 64)
-          name = wide ? "dense_64x128_stream" : "dense_64x64_stream";
+          name = !wide ? "dense_64x64_stream"
+                       : long_range ? "dense_64x128_stream_4w" : "dense_64x128_stream";
         else
-          name = wide ? "dense_128x128_stream" : "dense_128x64_stream";
+          name = !wide ? "dense_128x64_stream"
+                       : long_range ? "dense_128x128_stream_4w" : "dense_128x128_stream";
         break;
       }
       /* fall through */

@@ -185,6 +185,20 @@ def test_tiled_selection_uses_measured_tile_efficiency(lib):
         assert b.dg_instance_name(1, rows, n, k, g) == "contig_256x256", (rows, n, k)
 
 
+def test_decode_selection(lib):
+    """Decode shapes (all rows in one tile) take the split-K instances: 128-column tiles
+    unless their grid would leave more than a quarter of the CUs idle, and the 4-wave
+    build of the 128-column tile when the ranges average 16 K blocks or more."""
+    from moe_grouped_gemm_lhs_amd import binding as b
+    want = {(64, 2112, 7168): "dense_64x64_stream", (64, 24576, 1536): "dense_64x128_stream",
+            (64, 7168, 16384): "dense_64x128_stream_4w", (64, 4096, 7168): "dense_64x128_stream",
+            (128, 2112, 7168): "dense_128x64_stream", (128, 32768, 512): "dense_128x128_stream",
+            (128, 7168, 16384): "dense_128x128_stream_4w",
+            (128, 4096, 7168): "dense_128x128_stream", (128, 7168, 2048): "dense_128x64_stream"}
+    for (m, n, k), name in want.items():
+        assert b.dg_instance_name(0, m, n, k, 1) == name, (m, n, k)
+
+
 def test_masked_selection(lib):
     """Masked calls whose groups each fit one 128-row tile (at most 64 groups) and whose
     column tiles are fewer than the CUs take the split-K instances that schedule on the

@@ -137,8 +137,8 @@ def test_tiled_pipeline_across_items(case, ragged_n, monkeypatch):
     monkeypatch.delenv("DG_FORCE_INSTANCE")
 
 
-STREAM_INSTANCES = ["dense_64x64_stream", "dense_64x128_stream", "dense_128x64_stream",
-                    "dense_128x128_stream"]
+STREAM_INSTANCES = ["dense_64x64_stream", "dense_64x128_stream", "dense_64x128_stream_4w",
+                    "dense_128x64_stream", "dense_128x128_stream", "dense_128x128_stream_4w"]
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 64, 128 * 200), (128, 200, 16384), (1, 130, 128 * 64),
@@ -236,7 +236,8 @@ def test_formats_every_instance(a_fmt, b_fmt, monkeypatch):
     """Each dense instance forced with E5M2 operands."""
     from moe_grouped_gemm_lhs_amd import binding as b
     for name in ["dense_256x256", "dense_256x224", "dense_128x128", "dense_64x128_stream",
-                 "dense_64x64_stream", "dense_128x128_stream", "dense_128x64_stream"]:
+                 "dense_64x64_stream", "dense_128x128_stream", "dense_128x64_stream",
+                 "dense_128x128_stream_4w", "dense_64x128_stream_4w"]:
         monkeypatch.setenv("DG_FORCE_INSTANCE", name)
         M = 333 if "stream" not in name else (50 if name.startswith("dense_64x") else 100)
         assert b.dg_instance_name(0, M, 400, 512, 1) == name
