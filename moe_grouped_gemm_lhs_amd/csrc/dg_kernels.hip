@@ -1272,9 +1272,10 @@ template <int FA, int FB> using Str64 = Cfg<64, 128, 2, 4, 5, true, FA, FB>;    
 template <int FA, int FB> using Str64n64 = Cfg<64, 64, 2, 4, 8, true, FA, FB>;   // 64 rows x 64 columns
 template <int FA, int FB> using Str128 = Cfg<128, 128, 2, 4, 4, true, FA, FB>;   // 128 rows x 128 columns
 template <int FA, int FB> using Str128n64 = Cfg<128, 64, 2, 4, 6, true, FA, FB>; // 128 rows x 64 columns
-// 4-wave builds of the 128-column tiles (one wave per SIMD, half the fragment reads from
-// LDS per K block) for ranges of 16 K blocks or more per workgroup: 128x7168x16384
-// 44.0 -> 39.7 us, 64x7168x16384 34.0 -> 33.3 us; on shorter ranges they lose 2-7%
+// 4-wave builds of the 128-column tiles (one wave per SIMD; per K block 64 KB of fragment
+// reads from LDS instead of 96, 48 instead of 64) for ranges of 16 K blocks or more per
+// workgroup: 128x7168x16384 44.0 -> 39.7 us, 64x7168x16384 34.0 -> 33.3 us; on shorter
+// ranges they lose 2-7%
 template <int FA, int FB> using Str128w4 = Cfg<128, 128, 2, 2, 4, true, FA, FB>;  // 64x64 per wave
 template <int FA, int FB> using Str64w4 = Cfg<64, 128, 2, 2, 5, true, FA, FB>;    // 32x64 per wave
 
