@@ -54,6 +54,11 @@
  *     its first use; every call leaves it zero filled again (a zero word marks a partial
  *     not yet written), so one workspace can serve calls of any shape in stream order.
  *     Two calls that may run concurrently must not share one workspace.
+ *   - Split-K calls (those with a workspace) have workgroups that wait, boundedly, for
+ *     one another's partial sums.  Their grid never exceeds the GPU's compute units, so
+ *     on a GPU the call has to itself they all run at once; if other work keeps one of
+ *     them from starting for longer than the wait's bound (well under a second), the
+ *     output elements that depend on it are written as NaN instead of the call hanging.
  */
 #ifndef DG_H_
 #define DG_H_
