@@ -140,30 +140,39 @@ def main():
         sA = torch.from_numpy(p.sA).to(dev)
         B = torch.from_numpy(p.B).to(dev)
         sB = torch.from_numpy(p.sB).to(dev)
+        mm = None
         if p.kind == "dense":
             B, sB = B.view(p.N, p.K), sB.view(nnb, nkb)
             C = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=dev)
-            fn = (lambda A=A, sA=sA, B=B, sB=sB, C=C:
-                  dg.dg_gemm_fp8_nt(A, sA, B, sB, C, workspace=ws, **fm))
+            ops = [A, sA, B, sB, C]
+            def make(A, sA, B, sB, C, fm=fm):
+                return lambda: dg.dg_gemm_fp8_nt(A, sA, B, sB, C, workspace=ws, **fm)
         elif p.kind == "contiguous":
             B, sB = B.view(p.G, p.N, p.K), sB.view(p.G, nnb, nkb)
             gi = torch.from_numpy(p.group_idx).to(dev)
             C = torch.empty((p.rows, p.N), dtype=torch.bfloat16, device=dev)
-            fn = (lambda A=A, sA=sA, B=B, sB=sB, gi=gi, C=C:
-                  dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, gi, C, workspace=ws, **fm))
+            ops = [A, sA, B, sB, gi, C]
+            def make(A, sA, B, sB, gi, C, fm=fm):
+                return lambda: dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, gi, C,
+                                                                 workspace=ws, **fm)
         else:
             A, sA = A.view(p.G, p.M, p.K), sA.view(p.G, p.M, nkb)
             B, sB = B.view(p.G, p.N, p.K), sB.view(p.G, nnb, nkb)
             mm = torch.from_numpy(p.masked_m).to(dev)
             C = torch.empty((p.G, p.M, p.N), dtype=torch.bfloat16, device=dev)
-            fn = (lambda A=A, sA=sA, B=B, sB=sB, mm=mm, C=C:
-                  dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, mm, C, workspace=ws, **fm))
+            ops = [A, sA, B, sB, mm, C]
+            def make(A, sA, B, sB, mm, C, fm=fm):
+                return lambda: dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, mm, C,
+                                                             workspace=ws, **fm)
+        fn = make(*ops)
+        # the same call over fresh copies of every operand (for timing without cache reuse)
+        clone = (lambda make=make, ops=ops: make(*[t.clone() for t in ops]))
         flops, nbytes = work_of(p)
         kind_id = {"dense": 0, "contiguous": 1, "masked": 2}[p.kind]
         inst = dg.dg_instance_name(kind_id, p.M if p.kind != "contiguous" else p.rows, p.N, p.K, p.G)
         problems.append(p)
-        calls.append(dict(name=I.case_name(case), fn=fn, flops=flops, bytes=nbytes,
-                          instance=inst, masked_m=mm if p.kind == "masked" else None))
+        calls.append(dict(name=I.case_name(case), fn=fn, clone=clone, flops=flops,
+                          bytes=nbytes, instance=inst, masked_m=mm))
     torch.cuda.synchronize()
     gen_s = time.time() - t0
     print(f"[bench] {len(calls)} shapes resident in HBM ({gen_s:.1f} s to generate)",
@@ -248,7 +257,7 @@ def main():
     dom = max(range(len(calls)), key=lambda i: per[i]["us"])
     d = per[dom]
     # ---- timed region 3: its launch duration without the per-launch event overhead
-    launch_us = _batch_launch_us(torch, stream, calls[dom]["fn"], args.steps, d["us"])
+    launch_us = _batch_launch_us(torch, stream, calls[dom], args.steps, d["us"])
     if hbm_bound:
         achieved = calls[dom]["bytes"] / (launch_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -346,8 +355,10 @@ def bench_quant(args, torch, np, dg, I, dev):
         S = torch.empty((srows, K // 128), dtype=torch.float32, device=dev)
         f = dg.dg_quantize_fp8_1x128 if kind == "1x128" else dg.dg_quantize_fp8_128x128
         nbytes = rows * K * 3 + S.numel() * 4
-        calls.append(dict(name=f"quant_{kind}_{rows}x{K}", fn=(lambda f=f, X=X, Q=Q, S=S:
-                                                             f(X, fmt, Q, S)),
+        make = (lambda X, Q, S, f=f: (lambda: f(X, fmt, Q, S)))
+        clone = (lambda make=make, X=X, Q=Q, S=S:
+                 make(X.clone(), torch.empty_like(Q), torch.empty_like(S)))
+        calls.append(dict(name=f"quant_{kind}_{rows}x{K}", fn=make(X, Q, S), clone=clone,
                           bytes=nbytes, instance=f"quant_{kind}", X=X, kind=kind))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
@@ -383,7 +394,7 @@ def bench_quant(args, torch, np, dg, I, dev):
         per.append((c["name"], round(us, 3), round(c["bytes"] / us / 1e3, 1)))
     total = sum(c["bytes"] for c in calls)
     dom = max(range(len(calls)), key=lambda i: per[i][1])
-    launch_us = _batch_launch_us(torch, stream, calls[dom]["fn"], args.steps, per[dom][1])
+    launch_us = _batch_launch_us(torch, stream, calls[dom], args.steps, per[dom][1])
     achieved = calls[dom]["bytes"] / (launch_us * 1e-6) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
@@ -452,20 +463,29 @@ def _profiled_traffic(instance, shape):
         return None
 
 
-def _batch_launch_us(torch, stream, fn, n, est_us):
-    """Mean duration of one launch of `fn`: n back-to-back launches queued behind a
+MALL_BYTES = 256 << 20           # MI355X Infinity Cache (memory-side, in front of HBM)
+
+
+def _batch_launch_us(torch, stream, call, n, est_us):
+    """Mean duration of one launch of a call: n back-to-back launches queued behind a
     device-side spin (so the host's launch latency is hidden), one pair of HIP events
     recorded on the launch stream around all of them; the gaps between consecutive
-    launches are included, the per-launch event overhead is not."""
+    launches are included, the per-launch event overhead is not.  The launches rotate
+    over copies of the call's operands, enough that twice the Infinity Cache's capacity
+    is touched between two reads of the same bytes, so no launch finds its inputs left
+    in that cache by an earlier one."""
+    r = min(16, max(1, -(-2 * MALL_BYTES // max(call["bytes"], 1)) + 1))
+    fns = [call["fn"]] + [call["clone"]() for _ in range(r - 1)]
     spin = _spin_cycles_for(torch, stream, 1.5 * n * est_us * 1e-6 + 50e-6)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     torch.cuda._sleep(spin)
     e0.record(stream)
-    for _ in range(n):
-        fn()
+    for i in range(n):
+        fns[i % r]()
     e1.record(stream)
     torch.cuda.synchronize()
+    del fns
     return 1e3 * e0.elapsed_time(e1) / n
 
 
