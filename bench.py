@@ -466,6 +466,12 @@ def _profiled_traffic(instance, shape):
 MALL_BYTES = 256 << 20           # MI355X Infinity Cache (memory-side, in front of HBM)
 
 
+def rotation_copies(nbytes):
+    """Operand sets a timed call rotates over: enough that the other sets' bytes between
+    two uses of one set exceed twice the Infinity Cache (at most 16 sets)."""
+    return min(16, -(-2 * MALL_BYTES // max(nbytes, 1)) + 1)
+
+
 def _batch_launch_us(torch, stream, call, n, est_us):
     """Mean duration of one launch of a call: n back-to-back launches queued behind a
     device-side spin (so the host's launch latency is hidden), one pair of HIP events
@@ -474,7 +480,7 @@ def _batch_launch_us(torch, stream, call, n, est_us):
     over copies of the call's operands, enough that twice the Infinity Cache's capacity
     is touched between two reads of the same bytes, so no launch finds its inputs left
     in that cache by an earlier one."""
-    r = min(16, max(1, -(-2 * MALL_BYTES // max(call["bytes"], 1)) + 1))
+    r = rotation_copies(call["bytes"])
     fns = [call["fn"]] + [call["clone"]() for _ in range(r - 1)]
     spin = _spin_cycles_for(torch, stream, 1.5 * n * est_us * 1e-6 + 50e-6)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
