@@ -59,15 +59,28 @@ __device__ __forceinline__ float amax_of(const float* x) {
   return m;
 }
 
+// Smallest scale whose quotients take the reciprocal path below.  From 2^-64 up, 1/scale
+// is finite and, for every quotient that can round to a non-zero fp8 code (|x/scale| >=
+// 2^-18), x >= 2^-82 and y*scale is a multiple of 2^-128, so the residual below is an
+// exact fp32 value; smaller quotients give the zero code whatever their last bits.
+constexpr float kMinReciprocalScale = 0x1p-64f;
+
 // x / scale rounded to nearest fp32, from a correctly rounded reciprocal r = 1/scale:
 // y = x*r is within an ulp of the quotient and the residual x - y*scale is exact (one
 // fma), so y + r*residual rounded once is the correctly rounded quotient (Markstein's
-// theorem; no overflow or underflow here: |x| <= amax = scale * FMAX).  The sign comes
-// from x (scale > 0), which also keeps the sign of a zero.
+// theorem; no overflow: |x| <= amax = scale * FMAX).  The sign comes from x (scale > 0),
+// which also keeps the sign of a zero.  Blocks with a scale under kMinReciprocalScale
+// (amax below FMAX * 2^-64: tiny and subnormal inputs, where 1/scale overflows or the
+// residual underflows) take the IEEE division instead; there a scale that underflowed to
+// zero gives +-inf (saturated below) and 0/0 a zero with the sign of x.
 __device__ __forceinline__ float div_by_scale(float x, float scale, float r) {
-  const float y = x * r;
-  const float e = __builtin_fmaf(-y, scale, x);
-  return __builtin_copysignf(__builtin_fmaf(e, r, y), x);
+  if (scale >= kMinReciprocalScale) {
+    const float y = x * r;
+    const float e = __builtin_fmaf(-y, scale, x);
+    return __builtin_copysignf(__builtin_fmaf(e, r, y), x);
+  }
+  const float q = x / scale;                      // correctly rounded fp32 division
+  return q != q ? __builtin_copysignf(0.0f, x) : q;
 }
 
 // Four codes: the quotients saturated to +-FMAX, then converted by the hardware's
@@ -128,7 +141,7 @@ quant_1x128_kernel(const void* X, uint8_t* Q, float* S, int64_t nblk, int nkb, i
     for (int off = LPB / 2; off >= 1; off >>= 1)
       amax = fmaxf(amax, __shfl_xor(amax, off, LPB));
     const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<FMT>();
-    const float rcp = 1.0f / scale;                        // correctly rounded
+    const float rcp = 1.0f / scale;      // correctly rounded (unused below 2^-64)
     if (b[u] < nblk) {
       store_codes<FMT, BF16>(Q, i[u], x[u], scale, rcp);
       if (l == 0) S[b[u]] = scale;
@@ -183,7 +196,7 @@ quant_128x128_kernel(const void* X, uint8_t* Q, float* S, int64_t rows, int nkb,
     amax = fmaxf(fmaxf(wave_max[k & 1][0], wave_max[k & 1][1]),
                  fmaxf(wave_max[k & 1][2], wave_max[k & 1][3]));
     const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<FMT>();
-    const float rcp = 1.0f / scale;                        // correctly rounded
+    const float rcp = 1.0f / scale;      // correctly rounded (unused below 2^-64)
     if (t == 0) S[b] = scale;
     const int64_t rb = b / nkb;
     const int64_t col = (b - rb * nkb) * kBlockK + lc, row0 = rb * kBlockK + lr;

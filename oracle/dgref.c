@@ -377,6 +377,16 @@ static float block_scale(float amax, int fmt)
     return amax == 0.0f ? 1.0f : amax / fmax;
 }
 
+/* x / scale as an IEEE fp32 division.  A non-zero amax gives a zero scale only when
+ * amax / FMAX underflows (fp32 blocks with amax at most FMAX * 2^-150); then x / 0 is
+ * +-infinity, which the encoder saturates, and 0 / 0 is read as a zero with the sign of
+ * x (the sign of a zero quotient follows x everywhere else too). */
+static float block_quotient(float x, float scale)
+{
+    float q = x / scale;
+    return isnan(q) ? copysignf(0.0f, x) : q;
+}
+
 /* X rows x K fp32 -> Q rows x K codes, S rows x K/128 scales.  Returns -1 for an
  * unknown format or K not a multiple of 128, else 0. */
 int dgref_quantize_1x128(const float *X, int64_t rows, int64_t K, int fmt, uint8_t *Q,
@@ -398,7 +408,7 @@ int dgref_quantize_1x128(const float *X, int64_t rows, int64_t K, int fmt, uint8
             scale = block_scale(amax, fmt);
             S[r * nkb + kb] = scale;
             for (k = 0; k < DGREF_BLOCK; ++k) {
-                float q = x[k] / scale;
+                float q = block_quotient(x[k], scale);
                 Q[r * K + kb * DGREF_BLOCK + k] = encode_fp8_nearest((double)q, fmt);
             }
         }
@@ -428,7 +438,7 @@ int dgref_quantize_128x128(const float *X, int64_t rows, int64_t K, int fmt, uin
         S[rb * nkb + kb] = scale;
         for (r = r0; r < r1; ++r)
             for (k = k0; k < k0 + DGREF_BLOCK; ++k) {
-                float q = X[r * K + k] / scale;
+                float q = block_quotient(X[r * K + k], scale);
                 Q[r * K + k] = encode_fp8_nearest((double)q, fmt);
             }
     }

@@ -91,6 +91,33 @@ def test_quantize_ties_zeros_saturation(fmt, kind):
     check(x, fmt, kind, torch.float32, "ties/zeros/saturation")
 
 
+# amax per block: ordinary, either side of the 2^-64 scale below which the kernel divides
+# instead of multiplying by 1/scale, tiny (1/scale overflows), bf16 subnormal; fp32 adds
+# subnormal blocks and blocks whose scale underflows to zero
+TINY_AMAX = [3.0, 1e-15, 448 * 2.0 ** -64 * 1.5, 448 * 2.0 ** -64 * 0.75, 1e-30, 3e-36, 1e-36,
+             5e-37, 1e-38, 1e-40]
+TINY_AMAX_F32 = [1e-42, 4e-43, 2e-45]
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+@pytest.mark.parametrize("kind", ["1x128", "128x128"])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_tiny_blocks(fmt, kind, dtype):
+    """Blocks whose amax is tiny or subnormal, codes and scales bit for bit against the
+    oracle (a subnormal scale overflows 1/scale; the kernel divides there)."""
+    amaxes = TINY_AMAX + (TINY_AMAX_F32 if dtype == "float32" else [])
+    rng = np.random.default_rng(17)
+    x = np.zeros((200, 128 * len(amaxes)), np.float32)
+    for j, a in enumerate(amaxes):
+        blk = (rng.uniform(-1.0, 1.0, (200, 128)) * a).astype(np.float32)
+        blk[::7, 5] = np.float32(a)
+        blk[::5, 9] = -np.float32(a)
+        blk[::3, 11] = 0.0
+        blk[1::3, 12] = -0.0
+        x[:, 128 * j:128 * (j + 1)] = blk
+    check(x, fmt, kind, getattr(torch, dtype), "tiny and subnormal blocks")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_quantize_then_gemm(fmt):
     """X -> 1x128 codes, W -> 128x128 codes on the GPU, then the GEMM: codes identical to
