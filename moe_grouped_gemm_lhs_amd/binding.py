@@ -127,23 +127,38 @@ def _ptr(t):
 
 
 def _stream(device, stream):
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+    """The launch stream as the hipStream_t handle the C calls take."""
+    return ctypes.c_void_p(_launch_stream(device, stream).cuda_stream)
 
 
-def _workspace(kind, rows, N, K, G, device, workspace):
+def _launch_stream(device, stream):
+    """The stream the call runs on: the one given, else the device's current stream."""
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
+def _workspace(kind, rows, N, K, G, device, workspace, stream):
+    """The caller's workspace, or one kept per (device, launch stream): allocated and
+    zero filled on the launch stream, so the fill is ordered before the call and calls
+    on different streams never share one (every call leaves it zero filled again).
+    Under graph capture each call gets a fresh one from the graph's memory, zero filled
+    by a kernel inside the graph."""
     need = dg_workspace_bytes(kind, rows, N, K, G)
     if workspace is not None:
         return workspace, workspace.numel() * workspace.element_size()
     if need == 0:
         return None, 0
-    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < need:
-        # zero filled once; every call leaves it zero filled again
-        ws = torch.zeros(need, dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+    with torch.cuda.stream(stream):
+        if torch.cuda.is_current_stream_capturing():
+            ws = torch.zeros(need, dtype=torch.uint8, device=device)
+            return ws, ws.numel()
+        key = (device.index, stream.cuda_stream)
+        with _lock:
+            ws = _workspaces.get(key)
+            if ws is None or ws.numel() < need:
+                # the previous one was used on this stream only, so the allocator may
+                # hand its memory out again in this stream's order
+                ws = torch.zeros(need, dtype=torch.uint8, device=device)
+                _workspaces[key] = ws
     return ws, ws.numel()
 
 
@@ -164,14 +179,15 @@ def dg_gemm_fp8_nt(A, sA, B, sB, C=None, *, a_format=None, b_format=None, worksp
     if C is None:
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     _check(C, "C", torch.bfloat16, (M, N), dev)
-    ws, wsb = _workspace(DG_DENSE, M, N, K, 1, dev, workspace)
+    st_ = _launch_stream(dev, stream)
+    ws, wsb = _workspace(DG_DENSE, M, N, K, 1, dev, workspace, st_)
     lib = load_library()
     if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3:
         st = lib.dg_gemm_fp8_nt(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C), M, N, K,
-                                _ptr(ws), wsb, _stream(dev, stream))
+                                _ptr(ws), wsb, ctypes.c_void_p(st_.cuda_stream))
     else:
         st = lib.dg_gemm_fp8_nt_ex(_ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), _ptr(C), M, N,
-                                   K, _ptr(ws), wsb, _stream(dev, stream))
+                                   K, _ptr(ws), wsb, ctypes.c_void_p(st_.cuda_stream))
     if st != 0:
         raise DGError(st, "dg_gemm_fp8_nt")
     return C
@@ -194,16 +210,17 @@ def dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, group_idx, C=None, *, a_format=
     if C is None:
         C = torch.zeros((M, N), dtype=torch.bfloat16, device=dev)
     _check(C, "C", torch.bfloat16, (M, N), dev)
-    ws, wsb = _workspace(DG_CONTIGUOUS, M, N, K, G, dev, workspace)
+    st_ = _launch_stream(dev, stream)
+    ws, wsb = _workspace(DG_CONTIGUOUS, M, N, K, G, dev, workspace, st_)
     lib = load_library()
     if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3:
         st = lib.dg_grouped_gemm_fp8_contiguous(
             _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(group_idx), _ptr(C), M, N, K, G,
-            _ptr(ws), wsb, _stream(dev, stream))
+            _ptr(ws), wsb, ctypes.c_void_p(st_.cuda_stream))
     else:
         st = lib.dg_grouped_gemm_fp8_contiguous_ex(
             _ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), _ptr(group_idx), _ptr(C), M, N, K, G,
-            _ptr(ws), wsb, _stream(dev, stream))
+            _ptr(ws), wsb, ctypes.c_void_p(st_.cuda_stream))
     if st != 0:
         raise DGError(st, "dg_grouped_gemm_fp8_contiguous")
     return C
@@ -226,16 +243,17 @@ def dg_grouped_gemm_fp8_masked(A, sA, B, sB, masked_m, C=None, *, a_format=None,
     if C is None:
         C = torch.zeros((G, cap, N), dtype=torch.bfloat16, device=dev)
     _check(C, "C", torch.bfloat16, (G, cap, N), dev)
-    ws, wsb = _workspace(DG_MASKED, cap, N, K, G, dev, workspace)
+    st_ = _launch_stream(dev, stream)
+    ws, wsb = _workspace(DG_MASKED, cap, N, K, G, dev, workspace, st_)
     lib = load_library()
     if fa == DG_FP8_E4M3 and fb == DG_FP8_E4M3:
         st = lib.dg_grouped_gemm_fp8_masked(
             _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(masked_m), _ptr(C), G, cap, N, K,
-            _ptr(ws), wsb, _stream(dev, stream))
+            _ptr(ws), wsb, ctypes.c_void_p(st_.cuda_stream))
     else:
         st = lib.dg_grouped_gemm_fp8_masked_ex(
             _ptr(A), fa, _ptr(sA), _ptr(B), fb, _ptr(sB), _ptr(masked_m), _ptr(C), G, cap, N,
-            K, _ptr(ws), wsb, _stream(dev, stream))
+            K, _ptr(ws), wsb, ctypes.c_void_p(st_.cuda_stream))
     if st != 0:
         raise DGError(st, "dg_grouped_gemm_fp8_masked")
     return C

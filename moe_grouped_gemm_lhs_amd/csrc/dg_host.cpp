@@ -30,11 +30,10 @@ DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 
 int log_enabled() {
-  static int v = -1;
-  if (v < 0) {
+  static const int v = [] {
     const char* e = getenv("DG_LOG");
-    v = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
-  }
+    return (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+  }();
   return v;
 }
 
@@ -163,7 +162,7 @@ const Instance* select_instance(int kind, int64_t rows_or_cap, int64_t N, int64_
           {"256x256", 256, 256, 1.0}, {"256x224", 256, 224, eff224}, {"256x160", 256, 160, 0.80},
           {"128x128", 128, 128, 0.6}};
       double best = 1e300;
-      static char buf[64];
+      char buf[64];   // per call: concurrent calls from several host threads are fine
       for (const Opt& o : opts) {
         snprintf(buf, sizeof(buf), "%s_%s", pre, o.suffix);
         if (!find_instance(buf, fa, fb)) continue;
@@ -206,8 +205,8 @@ bool fill_tiles(GemmArgs& a, const Instance* in, int kind) {
 
 size_t workspace_for(const Instance* in, const GemmArgs& a) {
   if (!in) return 0;
-  if (in->mode == dg::kModeStream)   // two partial tiles per workgroup
-    return (size_t)dg::kStreamGrid * 2 * in->bm * in->bn * sizeof(float);
+  if (in->mode == dg::kModeStream)   // arrival counters, two partial tiles per workgroup
+    return dg::kArrivalBytes + (size_t)dg::kStreamGrid * 2 * in->bm * in->bn * sizeof(float);
   return 0;
 }
 
@@ -219,7 +218,8 @@ dg_status run(int kind, int fa, int fb, GemmArgs& a, void* workspace, size_t wor
   const size_t ws = workspace_for(in, a);
   if (ws > 0) {
     if (!workspace || workspace_bytes < ws || !aligned(workspace, 16)) return DG_ERR_WORKSPACE;
-    a.partial = (float*)workspace;
+    a.arrivals = (int*)workspace;
+    a.partial = (float*)((uint8_t*)workspace + dg::kArrivalBytes);
   }
   if (in->mode == dg::kModeStream && !a.partial)
     return DG_ERR_WORKSPACE;

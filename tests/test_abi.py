@@ -214,3 +214,32 @@ def test_masked_selection(lib):
         "stream" not in b.dg_instance_name(2, 128, 4096, 7168, 65)
     assert b.dg_workspace_bytes(2, 128, 4096, 7168, 4) > 0
     assert b.dg_workspace_bytes(2, 256, 4096, 7168, 4) == 0
+
+
+def test_selection_is_reentrant_across_host_threads(lib):
+    """dg_instance_name and dg_workspace_bytes called from 8 host threads at once give the
+    same answers as single-threaded calls (ctypes releases the GIL around each call)."""
+    import threading
+    shapes = []
+    for kind in (0, 1, 2):
+        for rows in (64, 128, 1024, 4096, 32768):
+            for n, k in ((2112, 7168), (7168, 2048), (4096, 7168), (24576, 1536)):
+                shapes.append((kind, rows, n, k, 4))
+    want = [(lib.dg_instance_name(*s), lib.dg_workspace_bytes(*s)) for s in shapes]
+    errors = []
+
+    def worker(t):
+        for rep in range(40):
+            order = shapes[t::3] + shapes
+            for s in order:
+                got = (lib.dg_instance_name(*s), lib.dg_workspace_bytes(*s))
+                if got != want[shapes.index(s)]:
+                    errors.append((s, got))
+                    return
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
