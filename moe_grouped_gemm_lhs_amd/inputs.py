@@ -207,11 +207,15 @@ def random_contiguous_sizes(seed: int, G: int = 8, align: int = 128, max_blocks:
     return [int(v) * align for v in rng.integers(1, max_blocks + 1, size=G)]
 
 
+def masked_counts(G: int, cap: int, seed: int) -> np.ndarray:
+    """The masked workload's per-group valid-row counts, uniform on [0, cap]."""
+    return np.random.default_rng(seed).integers(0, cap + 1, size=G).astype(np.int32)
+
+
 def make_masked(G: int, cap: int, N: int, K: int, seed: int, masked_m=None,
                 a_fmt: str = "e4m3", b_fmt: str = "e4m3") -> Problem:
     if masked_m is None:
-        rng = np.random.default_rng(seed)
-        masked_m = rng.integers(0, cap + 1, size=G)
+        masked_m = masked_counts(G, cap, seed)
     masked_m = np.asarray(masked_m, dtype=np.int32)
     a = normal_matrix(seed, _TAG_A, G * cap, K)
     A, sA = quantize_1x128(a, a_fmt)

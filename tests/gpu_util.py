@@ -111,18 +111,18 @@ def oracle_full(p, c_init_bits=None, group_idx=None, masked_m=None):
 
 
 def sample_rows(p, written, per_group=24, seed=0):
-    """Rows to check at full size: the first and last rows of every 128-row block edge
-    near group starts/ends, plus random written rows."""
+    """Rows to check at full size: the first and the last written row of every 128-row
+    block that has written rows (routing goes by 128-row blocks, so a block computed
+    with the wrong group's B, or not at all, shows in them), plus random written rows."""
     rng = np.random.default_rng(seed)
     w = np.nonzero(written)[0]
     if w.size <= 4 * per_group:
         return w
     picks = set()
-    picks.update(w[:4].tolist())
-    picks.update(w[-4:].tolist())
-    # block boundaries (tile edges)
-    for m in w:
-        if m % 128 in (0, 127) and rng.random() < 0.05:
-            picks.add(int(m))
+    blocks = w // 128
+    first = np.r_[True, blocks[1:] != blocks[:-1]]
+    last = np.r_[blocks[1:] != blocks[:-1], True]
+    picks.update(w[first].tolist())
+    picks.update(w[last].tolist())
     picks.update(rng.choice(w, size=min(w.size, 4 * per_group), replace=False).tolist())
     return np.array(sorted(picks), dtype=np.int64)

@@ -41,6 +41,9 @@ def check_sampled(p, what, seed=0):
     # routing: exactly the written rows changed; every other row keeps the sentinel
     untouched = c_gpu[~w]
     assert np.all(untouched == SENTINEL), f"{what}: rows outside the routing were written"
+    # and every written row was written in full (no output value is near -6.2e18)
+    missed = np.argwhere(c_gpu[w] == SENTINEL)
+    assert missed.size == 0, f"{what}: {len(missed)} written elements still hold the sentinel"
     rows = gu.sample_rows(p, w, seed=seed)
     if rows.size == 0:
         return
@@ -146,7 +149,8 @@ STREAM_INSTANCES = ["dense_64x64_stream", "dense_64x128_stream", "dense_64x128_s
 def test_stream_k_shared_tiles(M, N, K, monkeypatch):
     """Split-K decode instances: tiles shared by up to ~200 workgroups (one 64-column tile
     over 200 K blocks), ragged N, a single row, every stream instance that fits the rows;
-    the workspace must be zero filled again after every call."""
+    the workspace's arrival counters must be zero again after every call, and two calls
+    give identical bits."""
     from moe_grouped_gemm_lhs_amd import binding as b
     p = I.make_dense(M, N, K, seed=M + N + K // 128)
     A, sA, B, sB = gu.device_operands(p)
@@ -159,11 +163,15 @@ def test_stream_k_shared_tiles(M, N, K, monkeypatch):
         assert b.dg_instance_name(0, M, N, K, 1) == name
         need = b.dg_workspace_bytes(0, M, N, K, 1)
         ws = torch.zeros(need, dtype=torch.uint8, device=gu.DEV)
+        first = None
         for rep in range(2):     # the second call reuses the workspace the first left
             gu.say(f"[case] stream {name} {M}x{N}x{K} call {rep}")
             c_gpu = gu.run_gpu(p, ops=(A, sA, B, sB), workspace=ws)
             assert_within_tolerance(c_gpu, c_ref, written, f"{name} {M}x{N}x{K}")
             assert not ws.cpu().numpy().any(), f"{name}: workspace not left zero filled"
+            if first is None:
+                first = c_gpu
+            assert np.array_equal(c_gpu, first), f"{name}: two calls differ"
     monkeypatch.delenv("DG_FORCE_INSTANCE")
 
 
@@ -179,8 +187,8 @@ MASKED_STREAM_INSTANCES = ["masked_128x128_stream", "masked_128x64_stream"]
 ])
 def test_masked_stream_k(G, cap, N, K, mm, monkeypatch):
     """Split-K masked instances (the schedule is built on the device from masked_m): every
-    written row within tolerance, every other row untouched, the workspace left zero
-    filled after each of two calls; all-zero counts write nothing."""
+    written row within tolerance, every other row untouched, the workspace's arrival
+    counters zero again after each of two calls; all-zero counts write nothing."""
     from moe_grouped_gemm_lhs_amd import binding as b
     if mm is None:
         mm = np.random.default_rng(G + cap).integers(0, cap + 1, size=G)
@@ -460,3 +468,89 @@ def test_graph_capture_replays_with_new_counts():
         assert_within_tolerance(got, ref, w, f"graph replay {counts}")
         got_d = dC.view(torch.int16).cpu().numpy().view(np.uint16)
         assert_within_tolerance(got_d, ref_dense, np.ones_like(got_d, bool), "graph replay dense")
+
+
+def test_auto_workspace_on_side_streams():
+    """Split-K decode calls without a workspace argument, launched on two side streams
+    (neither the current stream) back to back and concurrently: each stream gets its own
+    workspace, zero filled on that stream before the call; every result matches the
+    oracle."""
+    from moe_grouped_gemm_lhs_amd import binding as dg
+    probs = [I.make_dense(64, 2112, 2048, seed=48), I.make_dense(128, 4096, 1024, seed=49)]
+    assert all("stream" in dg.dg_instance_name(0, p.M, p.N, p.K, 1) for p in probs)
+    refs = [gu.oracle_full(p) for p in probs]
+    ops = [gu.device_operands(p) for p in probs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        gu.say(f"[case] auto workspace on side streams, round {rep}")
+        outs = []
+        for p, o, s in zip(probs, ops, streams):
+            s.wait_stream(torch.cuda.current_stream())
+            C = torch.empty((p.M, p.N), dtype=torch.bfloat16, device=gu.DEV)
+            with torch.cuda.stream(s):
+                C.zero_()
+            dg.dg_gemm_fp8_nt(*o, C, stream=s)
+            dg.dg_gemm_fp8_nt(*o, C, stream=s)      # the second call reuses the workspace
+            outs.append(C)
+        torch.cuda.synchronize()
+        for p, C, ref in zip(probs, outs, refs):
+            got = C.view(torch.int16).cpu().numpy().view(np.uint16)
+            assert_within_tolerance(got, ref, np.ones_like(got, bool), f"side stream {p.M}")
+
+
+# --------------------------------------------- routing at workload size, every row exact
+_SMALL_INTS = np.arange(-4, 5)
+
+
+def _one_hot_problem(case):
+    """The case's routing (group sizes or masked_m) and shapes with integer-valued inputs:
+    A entries uniform on {-4..4}, unit scales, and for group g a one-hot B_g whose row n
+    has its 1 at column p_g(n) = (7n + 131g + 1) mod K.  Then C[m, n] = A[m, p_g(n)]
+    exactly, for the group g that row m belongs to; p_g(n) differs between groups for
+    every n, so a row computed with another group's B gets other integers."""
+    N, K = case["N"], case["K"]
+    if case["kind"] == "contiguous":
+        G, rows = len(case["sizes"]), sum(case["sizes"])
+    else:
+        G, rows = case["G"], case["G"] * case["cap"]
+    rng = np.random.default_rng(case["seed"] + 500)
+    a_codes = e4m3_codes_of(_SMALL_INTS.astype(np.float64))
+    A = a_codes[rng.integers(0, 9, size=(rows, K), dtype=np.uint8)]
+    cols = np.stack([(7 * np.arange(N) + 131 * g + 1) % K for g in range(G)])
+    B = np.zeros((G * N, K), np.uint8)
+    B[np.arange(G * N), cols.reshape(-1)] = e4m3_codes_of(np.ones(1))[0]
+    nkb, nnb = K // 128, -(-N // 128)
+    sA = np.ones((rows, nkb), np.float32)
+    sB = np.ones((G * nnb, nkb), np.float32)
+    if case["kind"] == "contiguous":
+        p = I.Problem("contiguous", rows, N, K, G, A, sA, B, sB,
+                      group_idx=I.group_sizes_to_idx(case["sizes"]), sizes=case["sizes"])
+    else:
+        p = I.Problem("masked", case["cap"], N, K, G, A, sA, B, sB,
+                      masked_m=I.masked_counts(G, case["cap"], case["seed"]))
+    return p, cols
+
+
+@pytest.mark.parametrize("case", I.contiguous_cases() + I.masked_cases(), ids=I.case_name)
+def test_routing_full_size_every_row(case):
+    """Grouped routing at the workload's full size: every written row bit-exact against
+    its integer product, every other row untouched."""
+    p, cols = _one_hot_problem(case)
+    gu.say(f"[case] one-hot routing {I.case_name(case)} rows={p.rows}")
+    got = gu.run_gpu(p)
+    w = gu.written_rows(p)
+    assert np.all(got[~w] == SENTINEL), "rows outside the routing were written"
+    # code -> bf16 bits of the decoded integer (exact)
+    lut = np.zeros(256, np.uint16)
+    codes = e4m3_codes_of(_SMALL_INTS.astype(np.float64))
+    lut[codes] = torch.tensor(_SMALL_INTS, dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if p.kind == "contiguous":
+        grp = p.group_idx
+    else:
+        grp = np.repeat(np.arange(p.G), p.M)
+    rows = np.nonzero(w)[0]
+    for r0 in range(0, rows.size, 4096):
+        r = rows[r0:r0 + 4096]
+        want = lut[p.A[r[:, None], cols[grp[r]]]]
+        bad = np.argwhere(got[r] != want)
+        assert bad.size == 0, f"{bad.shape[0]} elements differ, first at row {r[bad[0][0]]}"

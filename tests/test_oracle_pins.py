@@ -352,3 +352,39 @@ def test_p8_blockwise_einsum_with_scales():
     ref = (part * s).sum(axis=2)
     assert np.allclose(acc, ref, rtol=1e-14, atol=0)
     assert np.all(np.abs(bf16_to_f64(C) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", FMT_PAIRS[1:])
+def test_p7_grouped_forms_with_e5m2_equal_dense_calls(a_fmt, b_fmt):
+    """The grouped forms' operand formats: with E5M2 for either or both operands
+    (random codes over the whole range, random scales), masked at full counts and
+    contiguous both equal per-group dense calls, which P2 pins for every format pair;
+    a swapped or dropped format in a grouped form changes the decoded values."""
+    rng = np.random.default_rng(29)
+    G, cap, N, K = 3, 40, 150, 256
+    nnb, nkb = -(-N // 128), K // 128
+    A = random_codes(rng, (G * cap, K), a_fmt)
+    B = random_codes(rng, (G * N, K), b_fmt)
+    sA = random_scales(rng, (G * cap, nkb))
+    sB = random_scales(rng, (G * nnb, nkb))
+    fm = dict(a_fmt=a_fmt, b_fmt=b_fmt)
+    dense = [oracle.gemm_fp8_nt(A[g * cap:(g + 1) * cap], sA[g * cap:(g + 1) * cap],
+                                B[g * N:(g + 1) * N], sB[g * nnb:(g + 1) * nnb], **fm)
+             for g in range(G)]
+    Cm = oracle.grouped_masked(A, sA, B, sB, np.full(G, cap, np.int32), G, cap, **fm)
+    # contiguous: the same rows, padded to 128-row segments with rows marked -1
+    rows = 128 * G
+    Ac = np.zeros((rows, K), np.uint8)
+    sAc = np.ones((rows, nkb), np.float32)
+    gi = np.full(rows, -1, np.int32)
+    for g in range(G):
+        Ac[128 * g:128 * g + cap] = A[g * cap:(g + 1) * cap]
+        sAc[128 * g:128 * g + cap] = sA[g * cap:(g + 1) * cap]
+        gi[128 * g:128 * g + cap] = g
+    Cc = oracle.grouped_contiguous(Ac, sAc, B, sB, gi, G, **fm)
+    for g in range(G):
+        assert np.array_equal(Cm[g * cap:(g + 1) * cap], dense[g])
+        assert np.array_equal(Cc[128 * g:128 * g + cap], dense[g])
+    # and the formats matter: reading the operands as E4M3 gives other values
+    other = oracle.gemm_fp8_nt(A[:cap], sA[:cap], B[:N], sB[:nnb])
+    assert not np.array_equal(other, dense[0])
