@@ -10,15 +10,17 @@ namespace dg {
 
 constexpr int kBlockK = 128;       // depth of one scaled K block
 constexpr int kAlignM = 128;       // contiguous-layout row alignment
-// Stream-K workspace: two fp32 partial tiles per workgroup, stored bit-inverted (zero
-// means "not written"); it must be zero filled before the first call, and every call
-// leaves it zero filled.
 // Stream-K instances run at most this many workgroups.
 constexpr int kStreamGrid = 256;
-// Bound on a contributor's wait for the other partials of its tile: polls of about
-// 0.1-2 us each, so well under a second; a legitimate wait is a few microseconds.  A
-// fragment whose wait runs out is stored as NaN.
-constexpr int kSpinLimit = 1 << 16;
+// Stream-K workspace: one 8-byte record per (shared tile, wave) for up to kStreamGrid
+// shared tiles of 8 waves (arrival count and completed parts), then two fp32 partial
+// tiles per workgroup, stored bit-inverted (a zero word means "not written yet").  All
+// of it must be zero filled before the first call, and every call leaves it zero filled.
+constexpr int kArrivalBytes = kStreamGrid * 8 * 8;
+// Bound on a contributor's polls for the other partials of its part of a shared tile
+// (about a microsecond each); when it runs out the contributor leaves the part to the
+// last contributor to arrive, which never waits.
+constexpr int kHelperPolls = 2000;
 
 // Workgroups of a dense stream-K launch over `tiles` output tiles of `nkb` K blocks on
 // a grid of at most `g` (min(CUs, kStreamGrid)): whole tiles dealt out evenly when that
@@ -53,6 +55,7 @@ struct GemmArgs {
   const int32_t* group_idx;   // contiguous only
   const int32_t* masked_m;    // masked only
   float* partial;             // stream-K fp32 partial tiles (workspace), or nullptr
+  int* arrivals;              // stream-K arrival counters per shared tile (workspace)
   int rows;                   // dense M, contiguous M_total, masked cap
   int N, K, G;
   int nkb;                    // K / 128

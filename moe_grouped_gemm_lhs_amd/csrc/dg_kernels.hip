@@ -161,8 +161,9 @@ __device__ __forceinline__ int load_uniform(const int32_t* p, long i) {
 }
 
 // Split-K partials are stored bit-inverted, so that an all-zero word marks a slot not
-// yet written.  The only value whose inverse is zero, the NaN with every bit set, is
-// first replaced by another NaN.
+// yet written (the workspace's partial slots start zero filled and every call leaves
+// them so).  The only value whose inverse is zero, the NaN with every bit set, is first
+// replaced by another NaN.
 __device__ __forceinline__ v4i encode_partial(v4f v) {
   v4i u = __builtin_bit_cast(v4i, v);
 #pragma unroll
@@ -171,8 +172,8 @@ __device__ __forceinline__ v4i encode_partial(v4f v) {
 }
 __device__ __forceinline__ v4f decode_partial(v4i u) { return __builtin_bit_cast(v4f, ~u); }
 
-// Cache policy of the polling loads: sc1 (device coherent) plus the intrinsic's volatile
-// bit, so that the compiler keeps every poll inside its loop.
+// Cache policy of loads that poll for another workgroup's partials: sc1 (device
+// coherent) plus the intrinsic's volatile bit, so that each poll stays inside its loop.
 constexpr int kPollAux = (int)0x80000010u;
 
 // One MFMA operand fragment from LDS (32 bytes per lane: chunks q and q+4 of the lane's
@@ -895,20 +896,14 @@ gemm_fp8_kernel(GemmArgs p) {
 // load pipeline runs through a workgroup's whole range, across tile boundaries.
 // A tile whose K blocks all fall in one workgroup's range is stored as bf16 directly.
 // A tile shared by n workgroups (its contributors, consecutive in workgroup order) is
-// reduced deterministically and in parallel, with no atomics: each contributor writes its
-// fp32 partial in fragment order (one contiguous 1 KB block per 16x16 sub-tile) with
-// device-coherent (sc1) stores, every value stored bit-inverted so that a zero word
-// means "not written yet" (the workspace starts zero filled).  The tile's reducers are
-// the contributors whose range ends inside it (all but the last contributor, unless that
-// one's range ends with the tile); after its loop, each reducer takes every nr-th
-// fragment of the tile (nr reducers): it polls each contributor's slot until all of its
-// words are non-zero, sums the contributors in workgroup order, stores those fragments
-// as bf16 and writes zeros back, which leaves the workspace zero filled for the next
-// call.  Every workgroup writes all its partials
-// before it waits on any, and the persistent grid never exceeds the CU count with one
-// workgroup per CU (the LDS budget admits no second), so all contributors are resident
-// and every wait ends; the wait is bounded all the same.  A workgroup holds at most two
-// shared tiles: the first and the last of its range.
+// reduced deterministically with no waiting: each contributor stores its fp32 partial in
+// fragment order (one contiguous 1 KB block per 16x16 sub-tile) with device-coherent
+// (sc1) stores and, once they are complete, adds one to the tile's arrival counter (a
+// device-scope atomic); the contributor that finds n-1 there is the last, resets the
+// counter to zero and sums the n partials in workgroup order, then stores bf16.  No
+// workgroup ever waits for another, so the result does not depend on which workgroups
+// run at the same time.  A workgroup holds at most two shared tiles: the first and the
+// last of its range.
 // Where the stream-K iterations of the masked form live.  Lane l of every wave holds
 // group l's row tiles under its masked_m (clamped to [0, cap]) and, scanned over the
 // lanes, the first tile of group l + 1 (the groups' tiles are row-major: all column tiles
@@ -983,6 +978,139 @@ __device__ __forceinline__ void masked_tile(const GemmArgs& p, const MaskedPlan&
   x.nb_first = x.n0 / kBlockK;
 }
 
+// Reduction of a shared stream-K tile, spread over its contributors, none of which
+// depends on another making progress.  The tile's fragments are split into P parts
+// (fragment f of wave w is in part (w*TI*TJ + f) % P, P = min(reducers, fragments, 32),
+// the reducers being the contributors whose range ends inside the tile), and
+// contributor c < P reduces part c: it polls the contributors' slots for the part
+// (their stores are the signal: a written word is never zero), boundedly, sums them in
+// workgroup order, stores bf16 and zeroes the slots.  Every contributor then counts its
+// arrival at the tile, with the bit of the part it completed, in one 64-bit atomic add on
+// the tile's record (arrivals in the high word, completed parts in the low).  The last to
+// arrive knows that every partial is stored and that nobody touches the record again:
+// it reduces the parts nobody completed (a contributor whose wait ran out leaves its part
+// to it) and clears the record.  Each part is summed in the same order whoever reduces
+// it.  All of this runs per wave: the fragments of wave w of every contributor form
+// their own reduction with their own record, so the waves of a workgroup never wait for
+// one another (a wave with no fragment in its part has completed it at once).
+//
+// This wave's fragments of the parts in `mask`, FCH fragments at a time, their partials
+// from CB contributors per batch of loads in flight (polled until every word is written,
+// at most `polls` times; slots past the buffer or of no fragment read zeros without
+// touching memory and count as written), summed in workgroup order and stored as bf16
+// (rows at or past `rows`, columns at or past N are not written).  With ZERO the slots
+// are zeroed instead.  Returns false if a poll ran out (nothing is zeroed then).
+template <class C, bool ZERO>
+__device__ __forceinline__ bool reduce_parts(int mask, int P, int n, int g_first, int first_slot,
+                                             __amdgpu_buffer_rsrc_t part_rsrc,
+                                             const GemmArgs& p, int row0, int rows, int n0,
+                                             int wave, int wm, int wn, int lane, int polls) {
+  constexpr int NF = C::TI * C::TJ;
+  constexpr int FCH = NF < 2 ? NF : 2;         // 16 loads in flight per poll
+  constexpr int CB = 8;
+  constexpr int WAVE_SLOT = NF * 64 * 4;                   // floats of one wave's partial
+  constexpr int kPastBuffer = 0x7FFFFF00;
+  const int l16 = lane & 15, q = lane >> 4;
+  int f = 0;
+#pragma unroll 1
+  for (;;) {
+    int fl[FCH];                                          // the chunk's fragments, or -1
+#pragma unroll
+    for (int k = 0; k < FCH; ++k) {
+      while (f < NF && !((mask >> ((wave * NF + f) % P)) & 1)) ++f;
+      fl[k] = f < NF ? f : -1;
+      f = f < NF ? f + 1 : f;
+    }
+    if (fl[0] < 0) break;
+    v4f sum[FCH];
+#pragma unroll
+    for (int k = 0; k < FCH; ++k) sum[k] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int c0 = 0; c0 < n; c0 += CB) {
+      // a contributor's slot for this tile: 0 if its range starts inside the tile (the
+      // tile is its first), else 1 (the tile is its last): only the first contributor's
+      // range can start before the tile
+      int off[CB][FCH];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        const int gg = g_first + c0 + u;
+        const int slot = c0 + u == 0 ? first_slot : 0;
+        const int base = ((gg * 2 + slot) * C::W + wave) * WAVE_SLOT * 4;
+#pragma unroll
+        for (int k = 0; k < FCH; ++k) {
+          off[u][k] = c0 + u < n && fl[k] >= 0 ? base + (fl[k] * 64 + lane) * 16 : kPastBuffer;
+        }
+      }
+      if constexpr (ZERO) {
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+#pragma unroll
+          for (int k = 0; k < FCH; ++k)
+            if (off[u][k] != kPastBuffer)
+              __builtin_amdgcn_raw_buffer_store_b128((v4i){0, 0, 0, 0}, part_rsrc, off[u][k], 0,
+                                                     16 /* sc1 */);
+        continue;
+      }
+      // slots of no contributor or fragment read zeros: they count as written
+      unsigned dead[CB][FCH];
+#pragma unroll
+      for (int u = 0; u < CB; ++u)
+#pragma unroll
+        for (int k = 0; k < FCH; ++k) dead[u][k] = off[u][k] == kPastBuffer ? ~0u : 0u;
+      v4i raw[CB][FCH];
+      bool ready = false;
+#pragma unroll 1
+      for (int poll = 0; poll < polls && !ready; ++poll) {
+        if (poll > 0) __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+#pragma unroll
+          for (int k = 0; k < FCH; ++k)
+            raw[u][k] = __builtin_amdgcn_raw_buffer_load_b128(part_rsrc, off[u][k], 0, kPollAux);
+        // the smallest word over all loads (unsigned; a dead slot counts as all ones) is
+        // zero iff some slot is not written yet: min/max arithmetic, one compare per poll
+        unsigned least = ~0u;
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+#pragma unroll
+          for (int k = 0; k < FCH; ++k) {
+            const v4i r = raw[u][k];
+            const unsigned m = min(min((unsigned)r.x, (unsigned)r.y), min((unsigned)r.z, (unsigned)r.w));
+            least = min(least, max(m, dead[u][k]));
+          }
+        ready = __builtin_amdgcn_ballot_w64(least == 0) == 0;
+      }
+      if (!ready) return false;
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        if (c0 + u >= n) break;
+#pragma unroll
+        for (int k = 0; k < FCH; ++k) sum[k] += decode_partial(raw[u][k]);
+      }
+    }
+    if constexpr (!ZERO) {
+#pragma unroll
+      for (int k = 0; k < FCH; ++k) {
+        if (fl[k] < 0) continue;
+        const int fi = fl[k] / C::TJ, fj = fl[k] - fi * C::TJ;
+        const int row = wm * C::WM + 16 * fi + l16;
+        const int col = n0 + wn * C::WN + 16 * fj + 4 * q;
+        if (row >= rows) continue;
+        uint16_t* dst = p.C + (size_t)(row0 + row) * p.N;
+        const v4f v = sum[k];
+        if (((p.N & 3) == 0) && col + 3 < p.N) {
+          *(uint2*)(dst + col) = make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < p.N) dst[col + e] = bf16_rne(v[e]);
+        }
+      }
+    }
+  }
+  return true;
+}
+
 template <class C>
 __device__ __forceinline__ long stream_start(long g, long W, long G) { return g * W / G; }
 
@@ -992,6 +1120,7 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   constexpr int TI = C::TI, TJ = C::TJ, STAGES = C::STAGES;
   constexpr int FRAG_FLOATS = 64 * 4;                        // one 16x16 fp32 sub-tile
   constexpr int WAVE_SLOT = TI * TJ * FRAG_FLOATS;           // one wave's partial
+  static_assert(C::W <= 8, "the workspace holds one arrival record per wave, 8 per tile");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
@@ -1039,6 +1168,7 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   cn.l16 = l16;
   cc = cn;
 
+  // partial slots: two per workgroup (the first and the last tile of its range)
   __amdgpu_buffer_rsrc_t part_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       p.partial, (short)0, (int)((size_t)G * 2 * C::W * WAVE_SLOT * 4), 0x00020000);
 
@@ -1120,110 +1250,76 @@ gemm_fp8_stream_kernel(GemmArgs p) {
     in_tile = 0;
   }
 
-  // ---- reduction of a shared tile.  It is split among its reducers: the contributors
-  // whose range ends inside it, i.e. all but the last one, unless that one's range ends
-  // with the tile too.  The last contributor stored its partial when it moved on to the
-  // next tile, so the reducers only wait for one another, and a workgroup reduces at most
-  // one tile: the last of its range.  Reducer r of nr takes fragments r, r + nr, ...;
-  // wave w takes the share's fragments w, w + W, ... two at a time; for each pair it
-  // fetches the contributors' 1 KB slots CB at a time with all loads in flight together
-  // (polled until written), sums them in workgroup order, zeroes the slots, and stores
-  // bf16.  Waves work independently: no barrier.
-  constexpr int F = C::W * TI * TJ;                        // fragments per tile
-  constexpr int CB = 8;                                    // contributors per fetch
-  constexpr int kPastBuffer = 0x7FFFFF00;                  // beyond part_rsrc's range
-  const int t_last = (int)((i_end - 1) / nkb);
-  const int sel = shared_tile[1] >= 0 ? 1 : 0;
-  const int t = shared_tile[1] >= 0 ? shared_tile[1] : (shared_tile[0] == t_last ? t_last : -1);
-  const int t_row0 = sel ? seg_row0[1] : seg_row0[0];
-  const int t_rows = sel ? seg_rows[1] : seg_rows[0];
-  const int t_n0 = sel ? seg_n0[1] : seg_n0[0];
-  if (t >= 0) {
-    const long x0 = (long)t * nkb, x1 = x0 + nkb - 1;
-    const long g_first = ((x0 + 1) * G + W - 1) / W - 1;
-    const long g_last = ((x1 + 1) * G + W - 1) / W - 1;
-    const int n = (int)(g_last - g_first + 1);
-    const int nr = n - 1 + (stream_start<C>(g_last + 1, W, G) == x1 + 1 ? 1 : 0);
-    const int me = (int)(g - g_first);                     // this workgroup's reducer index
-    const int fm = me < F ? (F - me + nr - 1) / nr : 0;   // fragments me, me+nr, ...
+  // ---- hand-off of the shared tiles (see reduce_parts), wave by wave: the waves of a
+  // workgroup never wait for one another and touch no LDS here.  Jobs 0 and 1: this
+  // wave's own part of the last and the first shared tile; then its arrival at both;
+  // jobs 2 and 3: the parts nobody completed, where this wave arrived last.
+  if (shared_tile[0] < 0 && shared_tile[1] < 0) return;
+  // per shared tile, once: first contributor, contributors, parts, this workgroup's
+  // index among the contributors, and the first contributor's slot
+  int gfv[2], nv[2], pv[2], cv[2], fsv[2];
+#pragma unroll
+  for (int sg = 0; sg < 2; ++sg) {
+    const long x0 = (long)(shared_tile[sg] < 0 ? 0 : shared_tile[sg]) * nkb, x1 = x0 + nkb - 1;
+    const long gf = ((x0 + 1) * G + W - 1) / W - 1;
+    const long gl = ((x1 + 1) * G + W - 1) / W - 1;
+    // the parts go to the contributors whose range ends inside the tile: the last
+    // contributor's range usually goes on into the next tiles (the tile is its first,
+    // stored long before), so it takes a part only when its range ends with the tile
+    const int nr = (int)(gl - gf) + (stream_start<C>(gl + 1, W, G) == x1 + 1 ? 1 : 0);
+    gfv[sg] = (int)gf;
+    nv[sg] = (int)(gl - gf + 1);
+    pv[sg] = min(nr, min(C::W * TI * TJ, 32));
+    cv[sg] = (int)(g - gf);
+    fsv[sg] = stream_start<C>(gf, W, G) < x0 ? 1 : 0;
+  }
+  bool polled = false;
+  int okmask = 0, left0 = 0, left1 = 0;
 #pragma unroll 1
-    for (int k = wave; k < fm; k += 2 * C::W) {
-      const bool two = k + C::W < fm;
-      const int f0 = me + nr * k, f1 = me + nr * (k + C::W);
-      v4f sum[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 1
-      for (int c0 = 0; c0 < n; c0 += CB) {
-        // slot offsets; unused ones lie beyond the buffer's range, where the buffer load
-        // returns zeros without touching memory, so every load is unconditional
-        int off[2][CB];
+  for (int k = 0; k < 4; ++k) {
+    if (k == 2) {
+      // this wave's partial stores are complete before its arrival is counted: a wave
+      // that polled has used loads issued after them (vmcnt retires in issue order)
+      if (!polled) wait_vmcnt<0>();
+      unsigned long long before[2] = {0ull, 0ull};
 #pragma unroll
-        for (int u = 0; u < CB; ++u) {
-          const long gg = g_first + c0 + u;
-          const bool live = c0 + u < n;
-          // slot 0 if gg's range starts inside tile t (gg*W/G >= t*nkb), else slot 1
-          const int sg = gg * W >= x0 * G ? 0 : 1;
-          const long base = (gg * 2 + sg) * F;
-          off[0][u] = live ? (int)(((base + f0) * 64 + lane) * 16) : kPastBuffer;
-          off[1][u] = live && two ? (int)(((base + f1) * 64 + lane) * 16) : kPastBuffer;
-        }
-        v4i raw[2][CB];
-        bool ready = false;
-#pragma unroll 1
-        for (int spin = 0; spin < kSpinLimit && !ready; ++spin) {
-          if (spin > 0) __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-          for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int u = 0; u < CB; ++u)
-              raw[r][u] = __builtin_amdgcn_raw_buffer_load_b128(part_rsrc, off[r][u], 0,
-                                                                kPollAux);
-          bool mine = true;
-#pragma unroll
-          for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int u = 0; u < CB; ++u) {
-              const bool ok = raw[r][u].x != 0 && raw[r][u].y != 0 && raw[r][u].z != 0 &&
-                              raw[r][u].w != 0;
-              mine = mine && (ok || off[r][u] == kPastBuffer);
-            }
-          ready = __builtin_amdgcn_ballot_w64(!mine) == 0;
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-          for (int u = 0; u < CB; ++u) {
-            if (off[r][u] == kPastBuffer) continue;
-            // a wait that ran out leaves the fragment NaN
-            sum[r] += ready ? decode_partial(raw[r][u])
-                            : (v4f){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                                    __builtin_nanf("")};
-            __builtin_amdgcn_raw_buffer_store_b128((v4i){0, 0, 0, 0}, part_rsrc, off[r][u], 0,
-                                                   16 /* sc1 */);
-          }
+      for (int sg = 0; sg < 2; ++sg) {
+        const unsigned long long mine =
+            (1ull << 32) | ((okmask >> sg) & 1 ? 1ull << cv[sg] : 0ull);
+        if (lane == 0 && shared_tile[sg] >= 0)
+          before[sg] = __hip_atomic_fetch_add(
+              (unsigned long long*)p.arrivals + gfv[sg] * C::W + wave, mine, __ATOMIC_RELAXED,
+              __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        if (r == 1 && !two) break;
-        const int f = r == 0 ? f0 : f1;
-        const v4f v = sum[r];
-        const int sw = f / (TI * TJ), rem = f - sw * (TI * TJ);
-        const int fi = rem / TJ, fj = rem - fi * TJ;
-        const int swm = sw / C::WAVES_N, swn = sw - swm * C::WAVES_N;
-        const int row = swm * C::WM + 16 * fi + l16;
-        const int col = t_n0 + swn * C::WN + 16 * fj + 4 * q;
-        if (row < t_rows) {
-          uint16_t* dst = p.C + (size_t)(t_row0 + row) * p.N;
-          if (((p.N & 3) == 0) && col + 3 < p.N) {
-            const uint32_t lo = bf16x2_rne(v[0], v[1]);
-            const uint32_t hi = bf16x2_rne(v[2], v[3]);
-            *(uint2*)(dst + col) = make_uint2(lo, hi);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (col + e < p.N) dst[col + e] = bf16_rne(v[e]);
-          }
+      for (int sg = 0; sg < 2; ++sg) {
+        if (shared_tile[sg] < 0) continue;
+        const int hi = __builtin_amdgcn_readlane((int)(before[sg] >> 32), 0);
+        const int lo = __builtin_amdgcn_readlane((int)before[sg], 0);
+        if (hi == nv[sg] - 1) {                 // the last to arrive
+          const int mine_done = (okmask >> sg) & 1 ? 1 << cv[sg] : 0;
+          const int left = ((1 << pv[sg]) - 1) & ~(lo | mine_done);
+          if (sg) left1 = left; else left0 = left;
+          if (lane == 0)
+            __hip_atomic_store((unsigned long long*)p.arrivals + gfv[sg] * C::W + wave, 0ull,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
+    }
+    const int sg = (k & 1) ^ 1;              // the last shared tile first
+    if ((sg ? shared_tile[1] : shared_tile[0]) < 0) continue;
+    const int P = sg ? pv[1] : pv[0], c = sg ? cv[1] : cv[0];
+    const int mask = k < 2 ? (c < P ? 1 << c : 0) : (sg ? left1 : left0);
+    if (!mask) continue;
+    polled = polled || k < 2;
+    const int n = sg ? nv[1] : nv[0], gf = sg ? gfv[1] : gfv[0], fs = sg ? fsv[1] : fsv[0];
+    const int row0 = sg ? seg_row0[1] : seg_row0[0];
+    const int rows = sg ? seg_rows[1] : seg_rows[0];
+    const int n0 = sg ? seg_n0[1] : seg_n0[0];
+    if (reduce_parts<C, false>(mask, P, n, gf, fs, part_rsrc, p, row0, rows, n0, wave, wm, wn,
+                               lane, kHelperPolls)) {
+      reduce_parts<C, true>(mask, P, n, gf, fs, part_rsrc, p, 0, 0, 0, wave, wm, wn, lane, 0);
+      if (k < 2) okmask |= 1 << sg;
     }
   }
 }
