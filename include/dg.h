@@ -144,6 +144,23 @@ dg_status dg_grouped_gemm_fp8_masked(const uint8_t *A, const float *sA,
                                      int64_t G, int64_t cap, int64_t N, int64_t K,
                                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* dg_gemm_fp8_nt for callers that cannot allocate device memory (code under graph
+ * capture, serving loops that must not call hipMalloc): no workspace argument and no
+ * allocation of any kind.  Split-K calls use instead a workspace the library holds in a
+ * statically sized device array, one per GPU, kept until the process ends: at most
+ * 32 MiB + 64 KiB (enough for every shape this library accepts; a shape needing more
+ * would return DG_ERR_WORKSPACE).  On the first call for a device the array's address
+ * is looked up and, unless `stream` is being captured, the array is zeroed by a kernel
+ * on `stream` (make that first call outside graph capture); every call leaves it zero
+ * filled.  All calls on one GPU share the array:
+ * two such calls that may overlap in time (on different streams, or from different
+ * host threads without ordering) race and give undefined results; calls in one stream's
+ * order are fine.  Otherwise as dg_gemm_fp8_nt (E4M3 operands, same errors; DG_ERR_HIP
+ * if the array's address cannot be had). */
+dg_status dg_gemm_fp8_nt_noalloc(const uint8_t *A, const float *sA,
+                                 const uint8_t *B, const float *sB,
+                                 uint16_t *C, int64_t M, int64_t N, int64_t K, void *stream);
+
 /* The same three calls with explicit operand formats: a_format / b_format are
  * DG_FP8_E4M3 or DG_FP8_E5M2 (any pair), else DG_ERR_FORMAT.  The calls above are these
  * with both formats DG_FP8_E4M3.  Everything else (layouts, scales, routing, workspace,

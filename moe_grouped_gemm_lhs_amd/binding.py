@@ -60,6 +60,8 @@ def load_library():
         lib.dg_grouped_gemm_fp8_masked.restype = I
         lib.dg_grouped_gemm_fp8_masked.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64,
                                                    P, SZ, P]
+        lib.dg_gemm_fp8_nt_noalloc.restype = I
+        lib.dg_gemm_fp8_nt_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, P]
         lib.dg_gemm_fp8_nt_ex.restype = I
         lib.dg_gemm_fp8_nt_ex.argtypes = [P, I, P, P, I, P, P, I64, I64, I64, P, SZ, P]
         lib.dg_grouped_gemm_fp8_contiguous_ex.restype = I
@@ -190,6 +192,30 @@ def dg_gemm_fp8_nt(A, sA, B, sB, C=None, *, a_format=None, b_format=None, worksp
                                    K, _ptr(ws), wsb, ctypes.c_void_p(st_.cuda_stream))
     if st != 0:
         raise DGError(st, "dg_gemm_fp8_nt")
+    return C
+
+
+def dg_gemm_fp8_nt_noalloc(A, sA, B, sB, C=None, *, stream=None):
+    """dg_gemm_fp8_nt without a workspace argument: split-K calls use the library's
+    static per-GPU workspace (calls that overlap on one GPU race).  E4M3 operands."""
+    (A, fa), (B, fb) = _bytes_view(A, "A"), _bytes_view(B, "B")
+    if fa != DG_FP8_E4M3 or fb != DG_FP8_E4M3:
+        raise ValueError("dg_gemm_fp8_nt_noalloc takes E4M3 operands")
+    M, K = A.shape
+    N = B.shape[0]
+    dev = A.device
+    nkb, nnb = -(-K // 128), -(-N // 128)
+    _check(A, "A", torch.uint8, (M, K), dev)
+    _check(B, "B", torch.uint8, (N, K), dev)
+    _check(sA, "sA", torch.float32, (M, nkb), dev)
+    _check(sB, "sB", torch.float32, (nnb, nkb), dev)
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _check(C, "C", torch.bfloat16, (M, N), dev)
+    st = load_library().dg_gemm_fp8_nt_noalloc(_ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(C),
+                                               M, N, K, _stream(dev, stream))
+    if st != 0:
+        raise DGError(st, "dg_gemm_fp8_nt_noalloc")
     return C
 
 

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdg.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["dg_kernels.hip", "dg_quant.hip", "dg_host.cpp"]
+SOURCES = ["dg_kernels.hip", "dg_quant.hip", "dg_noalloc.hip", "dg_host.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -307,6 +307,34 @@ dg_status dg_gemm_fp8_nt(const uint8_t* A, const float* sA, const uint8_t* B, co
                            workspace_bytes, stream);
 }
 
+dg_status dg_gemm_fp8_nt_noalloc(const uint8_t* A, const float* sA, const uint8_t* B,
+                                 const float* sB, uint16_t* C, int64_t M, int64_t N, int64_t K,
+                                 void* stream) {
+  dg_status st = check_shape(dg::kDense, M, N, K, 1);
+  if (st != DG_OK) return st;
+  if (M == 0 || N == 0) return DG_OK;
+  if (!A || !sA || !B || !sB || !C) return DG_ERR_NULL;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(sA, 4) ||
+      !aligned(sB, 4))
+    return DG_ERR_ALIGN;
+  const size_t need = dg_workspace_bytes(dg::kDense, M, N, K, 1);
+  if (need > dg::scratch_capacity()) return DG_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    int num_cus = 0;
+    st = check_device(&num_cus);
+    if (st != DG_OK) return st;
+    if (dg::scratch_for_current_device(&ws, (hipStream_t)stream) != hipSuccess) {
+      (void)hipGetLastError();
+      return DG_ERR_HIP;
+    }
+  }
+  GemmArgs a{};
+  a.A = A; a.sA = sA; a.B = B; a.sB = sB; a.C = C;
+  a.rows = (int)M; a.N = (int)N; a.K = (int)K; a.G = 1;
+  return run(dg::kDense, DG_FP8_E4M3, DG_FP8_E4M3, a, ws, need, stream);
+}
+
 dg_status dg_grouped_gemm_fp8_contiguous_ex(const uint8_t* A, int a_format, const float* sA,
                                             const uint8_t* B, int b_format, const float* sB,
                                             const int32_t* group_idx, uint16_t* C,

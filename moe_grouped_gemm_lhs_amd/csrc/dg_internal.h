@@ -86,6 +86,12 @@ const Instance* instances(int* count);
 void launch_quantize(int block128x128, int fmt, int bf16, const void* X, uint8_t* Q, float* S,
                      int64_t rows, int64_t K, int num_cus, hipStream_t stream);
 
+// The library-owned split-K workspace of the current device (defined in
+// dg_noalloc.hip): its capacity in bytes, and its address (looked up, and zeroed unless
+// `stream` is capturing, on the first call for a device).
+size_t scratch_capacity();
+hipError_t scratch_for_current_device(void** out, hipStream_t stream);
+
 // Byte-matrix transposition (defined in dg_quant.hip); arguments already validated.
 void launch_transpose_u8(const uint8_t* X, uint8_t* Y, int64_t rows, int64_t cols,
                          hipStream_t stream);
