@@ -1,18 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the FP8 block-scaled NT GEMM on one MI355X.
 
-A step is one pass over every shape of the chosen workload, each shape one call of
-the library on inputs already resident in HBM.  Default workload: the dense decode
-shapes (M in {64,128} x the six DeepSeek-V3 (N,K) pairs of the flashmla.org/zh page's
-dense table), which are bound by HBM bandwidth.  Other workloads (--workload prefill,
-contiguous, masked, small) exist for measurement; the default line is the one reported.
+A step is one pass over every shape of a workload, each shape one call of the library
+on inputs already resident in HBM.  The default run measures the four GEMM workloads of
+the flashmla.org/zh page's tables in turn and prints one JSON line whose headline is
+the contiguous grouped workload (MoE prefill: {4x8192, 8x4096, 8 random} rows x
+(N,K) in {(4096,7168),(7168,2048)}, the largest single-GPU configuration, bound by the
+matrix cores) in FLOP/s; the dense decode (HBM-bound), dense prefill and masked grouped
+workloads ride along under "workloads", each with its own step rate and the roofline of
+its dominant kernel.  --workload picks one workload alone (also "quant", "small").
 
-Prints ONE JSON line with: the workload's aggregate throughput (algorithmic bytes per
-second for HBM-bound workloads, FLOP/s for MFMA-bound ones), a roofline object for the
-dominant kernel (its algorithmic bytes or FLOPs per launch over its mean launch time,
-measured with HIP events recorded on the launch stream around K back-to-back launches
-of it), and
-the CPU oracle timed on this host on a bounded sample of the same workload.
+Each roofline is the dominant (longest) kernel's algorithmic bytes or FLOPs per launch
+over its mean launch time, measured with HIP events recorded on the launch stream around
+back-to-back launches that rotate over copies of the operands (so none finds its inputs
+left in the Infinity Cache), against 8 TB/s or 5.0 PFLOP/s dense FP8.  The line also
+carries the GPU clock sampled while the headline's dominant kernel ran, the pages' own
+GB/s convention, and the CPU oracle timed on this host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -31,8 +34,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "contiguous", "masked", "small", "quant"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "decode", "prefill", "contiguous", "masked", "small", "quant"])
     ap.add_argument("--shapes", default="", help="comma-separated subset of shape indices")
     ap.add_argument("--formats", default="e4m3xe4m3",
                     choices=["e4m3xe4m3", "e5m2xe5m2", "e4m3xe5m2", "e5m2xe4m3"],
@@ -113,12 +116,64 @@ def main():
         del src, dst
     if args.workload == "quant":
         return bench_quant(args, torch, np, dg, I, dev)
-    cases = workload_cases(args.workload)
+
+    names = [args.workload] if args.workload != "all" else ["contiguous", "decode", "prefill",
+                                                             "masked"]
+    head = names[0]
+    results = {}
+    for name in names:
+        print(f"[bench] workload {name}", file=sys.stderr, flush=True)
+        results[name] = measure(name, args, torch, np, dg, I, dev, headline=name == head)
+        torch.cuda.empty_cache()
+    r = results[head]
+    fmt_note = "" if args.formats == "e4m3xe4m3" else f", operands {args.formats}"
+    line = {
+        "metric": "FP8 TFLOPS and HBM GB/s (as % of MI355X peak) per M,N,K / group shape",
+        "value": r["value"], "unit": r["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3" if args.formats == "e4m3xe4m3" else "fp8" + args.formats,
+        "data": "synthetic (seeded N(0,1), 1x128 / 128x128 e4m3fn block quantisation)",
+        "config": {"workload": WORKLOAD_TEXT[head] + fmt_note, "shapes": r["shapes"],
+                   "parallelism": "single GPU", "step": r["step"]},
+        "tflops": r["tflops"], "gbs": r["gbs"], "pages_gbs": r["pages_gbs"],
+        "roofline": r["roofline"],
+        "sclk_mhz": r.get("sclk_mhz"),
+        "cpu_baseline": r.get("cpu_baseline"),
+        "per_shape": r["per_shape"],
+    }
+    if len(names) > 1:
+        line["workloads"] = {
+            n: {k: results[n][k] for k in ("value", "unit", "ms_per_step", "tflops", "gbs",
+                                            "pages_gbs", "roofline", "per_shape")}
+            | {"workload": WORKLOAD_TEXT[n]}
+            for n in names[1:]}
+    if "masked_decode_latency_us" in r:
+        line["masked_decode_latency_us"] = r["masked_decode_latency_us"]
+    elif len(names) > 1 and "masked_decode_latency_us" in results.get("masked", {}):
+        line["workloads"]["masked"]["masked_decode_latency_us"] = \
+            results["masked"]["masked_decode_latency_us"]
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump(dict(line=line, detail={n: results[n]["detail"] for n in names}), f,
+                      indent=1)
+    print(json.dumps(line), flush=True)
+
+
+HBM_BOUND = {"decode", "masked", "small"}
+
+
+def measure(name, args, torch, np, dg, I, dev, headline=False):
+    """One workload: its step rate (a HIP graph of all its calls, replayed K times), each
+    call's duration (events around eager launches), the dominant call's launch time over
+    back-to-back launches, and, for the headline workload, the GPU clock while that call
+    runs and the CPU oracle on a sample."""
+    cases = workload_cases(name)
     a_fmt, b_fmt = args.formats.split("x")
     if (a_fmt, b_fmt) != ("e4m3", "e4m3"):
         cases = I.with_formats(cases, a_fmt, b_fmt)
-    if args.shapes:
-        keep = [int(s) for s in args.shapes.split(",")]
+    if args.shapes and args.workload != "all":
+        keep = [int(v) for v in args.shapes.split(",")]
         cases = [cases[i] for i in keep]
 
     # ---- inputs: generated on the host, made resident in HBM before timing
@@ -172,10 +227,10 @@ def main():
         inst = dg.dg_instance_name(kind_id, p.M if p.kind != "contiguous" else p.rows, p.N, p.K, p.G)
         problems.append(p)
         calls.append(dict(name=I.case_name(case), fn=fn, clone=clone, flops=flops,
-                          bytes=nbytes, instance=inst, masked_m=mm))
+                          bytes=nbytes, pages=pages_bytes_of(p), instance=inst, masked_m=mm))
     torch.cuda.synchronize()
     gen_s = time.time() - t0
-    print(f"[bench] {len(calls)} shapes resident in HBM ({gen_s:.1f} s to generate)",
+    print(f"[bench] {name}: {len(calls)} shapes resident in HBM ({gen_s:.1f} s to generate)",
           file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
@@ -228,17 +283,17 @@ def main():
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in calls] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    for s in range(args.steps):
+    for s_ in range(args.steps):
         torch.cuda._sleep(spin)
         for i, c in enumerate(calls):
-            ev[s][i][0].record(stream)
+            ev[s_][i][0].record(stream)
             c["fn"]()
-            ev[s][i][1].record(stream)
+            ev[s_][i][1].record(stream)
     torch.cuda.synchronize()
 
     per = []
     for i, c in enumerate(calls):
-        times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        times = [ev[s_][i][0].elapsed_time(ev[s_][i][1]) for s_ in range(args.steps)]
         us = 1e3 * float(np.mean(times))
         per.append(dict(name=c["name"], instance=c["instance"], us=round(us, 3),
                         us_median=round(1e3 * float(np.median(times)), 3),
@@ -246,8 +301,9 @@ def main():
                         gbs=round(c["bytes"] / us / 1e3, 1)))
     total_flops = sum(c["flops"] for c in calls)
     total_bytes = sum(c["bytes"] for c in calls)
+    total_pages = sum(c["pages"] for c in calls)
     step_s = ms_per_step / 1e3
-    hbm_bound = args.workload in ("decode", "masked", "small")
+    hbm_bound = name in HBM_BOUND
     if hbm_bound:
         value, unit = total_bytes / step_s / 1e9, "GB/s"
     else:
@@ -271,38 +327,79 @@ def main():
     roof["launch_us_event_pair"] = d["us"]
     roof["traffic"] = _profiled_traffic(d["instance"], d["name"])
 
-    graph_latency = None
-    if args.workload == "masked":
-        graph_latency = masked_graph_latency(torch, np, dev, problems, calls, args.steps)
+    out = {"value": round(value, 2), "unit": unit, "ms_per_step": round(ms_per_step, 4),
+           "shapes": len(calls),
+           "step": "one HIP graph of all shapes" if graph is not None else "eager launches",
+           "tflops": round(total_flops / step_s / 1e12, 2),
+           "gbs": round(total_bytes / step_s / 1e9, 1),
+           "pages_gbs": round(total_pages / step_s / 1e9, 1),
+           "roofline": roof,
+           "per_shape": [[q["name"], q["us"], q["tflops"], q["gbs"]] for q in per],
+           "detail": per}
+    if name == "masked":
+        out["masked_decode_latency_us"] = masked_graph_latency(torch, np, dev, problems, calls,
+                                                               args.steps)
+    if headline:
+        out["sclk_mhz"] = sclk_while_running(torch, calls[dom], seconds=2.0)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(problems, calls, args.cpu_budget_s, hbm_bound)
+    return out
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(problems, calls, args.cpu_budget_s, hbm_bound)
 
-    line = {
-        "metric": "FP8 TFLOPS and HBM GB/s (as % of MI355X peak) per M,N,K / group shape",
-        "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8e4m3" if args.formats == "e4m3xe4m3" else "fp8" + args.formats,
-        "data": "synthetic (seeded N(0,1), 1x128 / 128x128 e4m3fn block quantisation)",
-        "config": {"workload": WORKLOAD_TEXT[args.workload]
-                   + ("" if args.formats == "e4m3xe4m3" else f", operands {args.formats}"),
-                   "shapes": len(calls),
-                   "parallelism": "single GPU",
-                   "step": "one HIP graph of all shapes" if graph is not None else "eager launches"},
-        "tflops": round(total_flops / step_s / 1e12, 2),
-        "gbs": round(total_bytes / step_s / 1e9, 1),
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "per_shape": [[q["name"], q["us"], q["tflops"], q["gbs"]] for q in per],
-    }
-    if graph_latency is not None:
-        line["masked_decode_latency_us"] = graph_latency
-    if args.detail:
-        with open(args.detail, "w") as f:
-            json.dump(dict(line=line, per_shape=per), f, indent=1)
-    print(json.dumps(line), flush=True)
+def pages_bytes_of(p):
+    """The pages' GB/s convention for one call: FP8 A and B plus BF16 C, scales ignored,
+    every row (every capacity row in the masked layout) counted."""
+    from moe_grouped_gemm_lhs_amd import accounting as acc
+    if p.kind == "dense":
+        return acc.pages_bytes(1, p.M, p.N, p.K)
+    if p.kind == "contiguous":
+        return acc.pages_bytes(1, p.rows, p.N, p.K) + (p.G - 1) * p.N * p.K
+    return acc.pages_bytes(p.G, p.M, p.N, p.K)
+
+
+def sclk_while_running(torch, call, seconds=2.0):
+    """The GPU clock reported by rocm-smi, sampled every ~0.25 s while the call runs back
+    to back for about `seconds` (best effort: None when rocm-smi is unavailable)."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    smi = shutil.which("rocm-smi")
+    if smi is None:
+        return None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    call["fn"]()
+    e1.record()
+    torch.cuda.synchronize()
+    n = max(1, int(seconds / max(e0.elapsed_time(e1) * 1e-3, 1e-6)))
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                out = subprocess.run([smi, "--showclocks", "--json"], capture_output=True,
+                                     text=True, timeout=10).stdout
+                m = re.search(r'"sclk clock speed:":\s*"\((\d+)Mhz\)"', out)
+                if m:
+                    samples.append(int(m.group(1)))
+            except Exception:
+                return
+            stop.wait(0.25)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    for _ in range(n):
+        call["fn"]()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return None
+    samples.sort()
+    return {"median": samples[len(samples) // 2], "min": samples[0], "max": samples[-1],
+            "samples": len(samples),
+            "source": "rocm-smi --showclocks while the dominant kernel ran back to back"}
 
 
 def masked_graph_latency(torch, np, dev, problems, calls, steps):
@@ -513,11 +610,11 @@ def cpu_baseline(problems, calls, budget_s, hbm_bound, min_s=10.0):
     """Time the CPU oracle on a bounded sample of the workload: whole shapes in order,
     repeated until at least min_s of oracle time has been spent, and the leading rows of
     a shape when a whole one would overrun budget_s; throughput is scaled to the
-    metric's unit from the work actually done."""
+    metric's unit from the work actually done (a shape's bytes in proportion to the rows
+    done, so a partial shape does not count all of B)."""
     import oracle
-    from moe_grouped_gemm_lhs_amd import accounting as acc
 
-    done_s, done_flops, done_bytes = 0.0, 0, 0
+    done_s, done_flops, done_bytes = 0.0, 0, 0.0
     parts = {}
     passes = 0
     while done_s < min_s and done_s < budget_s:
@@ -543,17 +640,30 @@ def cpu_baseline(problems, calls, budget_s, hbm_bound, min_s=10.0):
             else:
                 r = r_probe
             done_s += dt
-            done_flops += acc.flops(r, p.N, p.K)
-            done_bytes += acc.algorithmic_bytes(r, p.N, p.K, 1)
+            done_flops += c["flops"] * r // max(rows, 1) if p.kind != "masked" else \
+                2 * r * p.N * p.K
+            done_bytes += c["bytes"] * r / max(rows, 1)
             parts[c["name"]] = f"{c['name']}:{r}/{rows} rows"
     if hbm_bound:
         value, unit = done_bytes / done_s / 1e9, "GB/s"
     else:
         value, unit = done_flops / done_s / 1e12, "TFLOP/s"
-    return {"value": round(value, 4), "unit": unit, "cores": oracle.threads(), "kind": "oracle",
+    return {"value": round(value, 5), "unit": unit, "cores": len(os.sched_getaffinity(0)),
+            "threads": oracle.threads(), "cpu": _cpu_model(), "kind": "oracle",
             "sample": f"{passes} pass(es) over " + "; ".join(parts.values())
                       + f" ({done_s:.1f} s of oracle time)",
             "tflops": round(done_flops / done_s / 1e12, 5)}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _oracle_rows(p, r):

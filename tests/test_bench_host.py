@@ -25,3 +25,20 @@ def test_rotation_copies_examples():
     assert bench.rotation_copies(121_466_880) == 6     # decode 128x7168x16384
     assert bench.rotation_copies(750_000_000) == 2     # a call larger than the cache
     assert bench.rotation_copies(300_000) == 16        # tiny calls: capped
+
+
+def test_pages_gbs_convention_reproduces_the_tables():
+    """The pages' GB/s column (FP8 A and B plus BF16 C, scales ignored, every capacity row
+    counted) from the bytes convention and their TFLOPS: three rows, one per table."""
+    class P:
+        pass
+
+    def gbs(p, rows, tflops):
+        return bench.pages_bytes_of(p) / (2 * rows * p.N * p.K / (tflops * 1e12)) / 1e9
+
+    d = P(); d.kind, d.M, d.N, d.K = "dense", 64, 2112, 7168
+    assert abs(gbs(d, 64, 206) - 1688) < 3
+    c = P(); c.kind, c.rows, c.G, c.N, c.K = "contiguous", 4 * 8192, 4, 4096, 7168
+    assert abs(gbs(c, 4 * 8192, 1297) - 418) < 3
+    m = P(); m.kind, m.G, m.M, m.N, m.K = "masked", 4, 256, 4096, 7168
+    assert abs(gbs(m, 4 * 256, 932) - 2064) < 3
