@@ -42,6 +42,8 @@ def parse():
                     help="operand formats A x B (the workloads are quantised to them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches, not a graph")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip sampling the GPU clock (2 s of back-to-back launches)")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--detail", default="", help="write per-shape details to this JSON file")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -340,7 +342,7 @@ def measure(name, args, torch, np, dg, I, dev, headline=False):
         out["masked_decode_latency_us"] = masked_graph_latency(torch, np, dev, problems, calls,
                                                                args.steps)
     if headline:
-        out["sclk_mhz"] = sclk_while_running(torch, calls[dom], seconds=2.0)
+        out["sclk_mhz"] = None if args.no_sclk else sclk_while_running(torch, calls[dom], 2.0)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(problems, calls, args.cpu_budget_s, hbm_bound)
     return out

@@ -716,23 +716,99 @@ __device__ __forceinline__ bool store_tile_direct(const v4f (&acc)[C::TI][C::TJ]
   return fast;
 }
 
-// A workgroup's work items: tiles slot, slot + G, ... that have rows to compute; the
-// contiguous form runs a tile once per group present in it (pass 0 and 1).
+// A workgroup's work items: items slot, slot + G, ... of the work list that have rows
+// to compute.  The list is the tiles in raster order; the contiguous form runs a tile once
+// per group present in it (pass 0 and 1).
 struct Work {
   int t;
   int pass;
   TileRef tr;
 };
 
+// Where the contiguous form's second passes go.  Run right after their first pass, by
+// the same workgroup, they pile on the few workgroups that drew a tile straddling two
+// groups (the random-size workload: 8 tiles for most workgroups, 9 or 10 for some).
+// Instead, when it pays and is cheap to set up, the second passes are appended to the
+// work list (pass-0 tiles first, then the second passes, row tile by row tile), where the
+// striding hands them to the workgroups that drew one tile fewer.  Each wave counts the
+// straddling row tiles with a vector scan of the group indices at kernel start (nothing
+// is in flight then); taking an appended item (at most kMaxAppended per workgroup) scans
+// again for its row tile.
+constexpr int kMaxAppended = 4;
+constexpr int kMaxScanRowTiles = 4096;
+
+// Does row tile r hold two 128-row blocks led by two different valid groups?
+template <class C>
+__device__ __forceinline__ bool straddles(const GemmArgs& p, int r) {
+  const int m0 = r * C::BM;
+  if (r >= p.tiles_m || m0 + kAlignM >= p.rows) return false;
+  const int l0 = p.group_idx[m0], l1 = p.group_idx[m0 + kAlignM];
+  return l0 >= 0 && l0 < p.G && l1 >= 0 && l1 < p.G && l0 != l1;
+}
+
+// With s < 0: the number of straddling row tiles; else the s-th of them.
+template <class C>
+__device__ __forceinline__ int straddle_scan(const GemmArgs& p, int s, int lane) {
+  int count = 0;
+  for (int r0 = 0; r0 < p.tiles_m; r0 += 64) {
+    const bool st = straddles<C>(p, r0 + lane);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(st);
+    const int n = (int)__builtin_popcountll(m);
+    if (s >= count && s < count + n) {
+      const int below = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((unsigned)m, 0));
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(st && below == s - count);
+      return r0 + (int)__builtin_ctzll(hit);
+    }
+    count += n;
+  }
+  return s < 0 ? count : 0;
+}
+
+// The work list's length: the tiles, plus the appended second passes when there are
+// some and at most kMaxAppended per workgroup (else each runs after its first pass).
 template <int KIND, class C>
-__device__ __forceinline__ void next_work(const GemmArgs& p, Work& w, int G) {
-  if (KIND == kContiguous && w.pass == 0 && w.tr.g2 >= 0) {
+__device__ __forceinline__ int work_total(const GemmArgs& p, int G, int lane) {
+  if (KIND != kContiguous || C::BM <= kAlignM || p.tiles_m > kMaxScanRowTiles)
+    return p.num_tiles;
+  const long extra = (long)straddle_scan<C>(p, -1, lane) * p.tiles_n;
+  return extra > (long)kMaxAppended * G ? p.num_tiles : p.num_tiles + (int)extra;
+}
+
+// The second pass of row tile rt, column tile tn (its tile straddles two groups).
+template <class C>
+__device__ __forceinline__ TileRef second_pass(const GemmArgs& p, int rt, int tn) {
+  TileRef r;
+  r.ok = 1;
+  r.g2 = -1;
+  r.m0 = rt * C::BM;
+  r.n0 = tn * C::BN;
+  r.row_base = 0;
+  r.rows = min(C::BM, p.rows - r.m0);
+  r.lead0 = load_uniform(p.group_idx, r.m0);
+  r.lead1 = load_uniform(p.group_idx, r.m0 + kAlignM);
+  r.g = uniform(r.lead1);
+  return r;
+}
+
+// APP: the second passes are appended (the list is `total` > num_tiles items long).
+template <int KIND, class C, bool APP>
+__device__ __forceinline__ void next_work(const GemmArgs& p, Work& w, int G, int total,
+                                          int lane) {
+  if (KIND == kContiguous && !APP && w.pass == 0 && w.tr.g2 >= 0) {
     w.pass = 1;
     return;
   }
   w.pass = 0;
-  for (w.t += G; w.t < p.num_tiles; w.t += G) {
+  for (w.t += G; w.t < total; w.t += G) {
+    if (APP && w.t >= p.num_tiles) {
+      const int e = w.t - p.num_tiles;
+      w.tr = second_pass<C>(p, uniform(straddle_scan<C>(p, e / p.tiles_n, lane)),
+                            e - (e / p.tiles_n) * p.tiles_n);
+      return;
+    }
     w.tr = locate_tile<KIND, C>(p, w.t);
+    if (APP) w.tr.g2 = -1;   // its second pass comes later
     if (w.tr.ok) return;
   }
 }
@@ -752,9 +828,10 @@ __device__ __forceinline__ void work_ctx(TileCtx& c, const GemmArgs& p, const Wo
 // math and the epilogue.  At any time the two touch different stages (the waits and
 // barriers order their reuse), and the restrict scopes let the compiler see that a read
 // of a stage does not depend on the copies in flight into the others.
-template <int KIND, class C>
+template <int KIND, class C, bool APP>
 __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __restrict__ rd,
-                                         const GemmArgs& p, TileCtx c, int G, int slot) {
+                                         const GemmArgs& p, TileCtx c, int G, int slot,
+                                         int nwork) {
   constexpr int TI = C::TI, TJ = C::TJ;
   constexpr int STAGES = C::STAGES;
   using E = Epi<C>;
@@ -764,7 +841,6 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
   constexpr int NST = DIRECT ? direct_stores<C>() : E::NST;
   static_assert((STAGES - 2) * C::PER_STAGE + (STAGES - 1) * NST < 64, "vmcnt range");
   const int nkb = p.nkb;
-  const int nwork = p.num_tiles;
   const int wave = c.wave;
 
   // w: the item being multiplied; wx: the next one, whose first K blocks are copied
@@ -772,11 +848,11 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
   // each item fills and drains its own pipeline)
   Work w = {slot - G, 1, {}};
   w.tr.g2 = -1;
-  next_work<KIND, C>(p, w, G);
+  next_work<KIND, C, APP>(p, w, G, nwork, c.lane);
   if (w.t >= nwork) return;
   work_ctx(c, p, w);
   Work wx = w;
-  next_work<KIND, C>(p, wx, G);
+  next_work<KIND, C, APP>(p, wx, G, nwork, c.lane);
   TileCtx cx = c;
   if (wx.t < nwork) work_ctx(cx, p, wx);
   const bool cross = nkb >= STAGES - 1;
@@ -848,7 +924,7 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
     fill = !cross;
     w = wx;
     c = cx;
-    next_work<KIND, C>(p, wx, G);
+    next_work<KIND, C, APP>(p, wx, G, nwork, c.lane);
     if (wx.t < nwork) work_ctx(cx, p, wx);
   }
 }
@@ -886,7 +962,16 @@ gemm_fp8_kernel(GemmArgs p) {
   const int G = gridDim.x;
   const int xcd_runs = (G % 8 == 0) ? 8 : 1;
   const int slot = (blockIdx.x % xcd_runs) * (G / xcd_runs) + blockIdx.x / xcd_runs;
-  tile_walk<KIND, C>(smem, smem, p, c, G, slot);
+  // two compiled walks: one that takes appended second passes, one with none of that
+  // code on the path of the (usual) lists without them
+  const int nwork = work_total<KIND, C>(p, G, c.lane);
+  if constexpr (KIND == kContiguous) {
+    if (nwork > p.num_tiles) {
+      tile_walk<KIND, C, true>(smem, smem, p, c, G, slot, nwork);
+      return;
+    }
+  }
+  tile_walk<KIND, C, false>(smem, smem, p, c, G, slot, nwork);
 }
 
 // ------------------------------------------------------------------------------------

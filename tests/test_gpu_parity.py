@@ -554,3 +554,25 @@ def test_routing_full_size_every_row(case):
         want = lut[p.A[r[:, None], cols[grp[r]]]]
         bad = np.argwhere(got[r] != want)
         assert bad.size == 0, f"{bad.shape[0]} elements differ, first at row {r[bad[0][0]]}"
+
+
+@pytest.mark.parametrize("sizes,N,K,full,what", [
+    # every third 128-row block starts a new group: a third of the 256-row tiles straddle
+    # two groups; their second passes are appended to the work list
+    ([384] * 40, 512, 256, True, "appended second passes"),
+    # 128-row groups: every tile straddles, more second passes than four per workgroup of a
+    # full-chip grid, so each runs right after its first pass (checked on the first and last
+    # row of every group, and on random rows)
+    ([128] * 128, 4352, 128, False, "second passes in place"),
+])
+def test_contiguous_straddling_tiles(sizes, N, K, full, what, monkeypatch):
+    """256-row contiguous tiles that hold two groups run once per group; both ways of
+    scheduling the second passes write every row of both groups, and nothing else."""
+    monkeypatch.setenv("DG_FORCE_INSTANCE", "contig_256x256")
+    p = I.make_contiguous(sizes, N, K, seed=len(sizes) + N)
+    label = f"contiguous {what} ({len(sizes)} groups, N={N})"
+    if full:
+        check_full(p, label)
+    else:
+        check_sampled(p, label, seed=len(sizes))
+    monkeypatch.delenv("DG_FORCE_INSTANCE")
