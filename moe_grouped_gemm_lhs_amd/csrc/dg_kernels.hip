@@ -1196,8 +1196,16 @@ __device__ __forceinline__ bool reduce_parts(int mask, int P, int n, int g_first
   return true;
 }
 
+// n / d for n >= 0, d > 0: a 32-bit unsigned division when both fit (every realistic
+// launch: a 64-bit division is a long emulated sequence), else a 64-bit one.
+__device__ __forceinline__ long udiv(long n, long d) {
+  if ((unsigned long long)n <= 0xFFFFFFFFull && (unsigned long long)d <= 0xFFFFFFFFull)
+    return (long)((unsigned)n / (unsigned)d);
+  return (long)((unsigned long long)n / (unsigned long long)d);
+}
+
 template <class C>
-__device__ __forceinline__ long stream_start(long g, long W, long G) { return g * W / G; }
+__device__ __forceinline__ long stream_start(long g, long W, long G) { return udiv(g * W, G); }
 
 template <int KIND, class C>
 __global__ void __launch_bounds__(C::NT)
@@ -1232,7 +1240,7 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   const long g = blockIdx.x;
   const long i_begin = g < G ? stream_start<C>(g, W, G) : 0;
   const long i_end = g < G ? stream_start<C>(g + 1, W, G) : 0;
-  const int t_first = (int)(i_begin / nkb);
+  const int t_first = (int)udiv(i_begin, nkb);
 
   TileCtx cn, cc;
   cn.A = p.A;
@@ -1346,8 +1354,8 @@ gemm_fp8_stream_kernel(GemmArgs p) {
 #pragma unroll
   for (int sg = 0; sg < 2; ++sg) {
     const long x0 = (long)(shared_tile[sg] < 0 ? 0 : shared_tile[sg]) * nkb, x1 = x0 + nkb - 1;
-    const long gf = ((x0 + 1) * G + W - 1) / W - 1;
-    const long gl = ((x1 + 1) * G + W - 1) / W - 1;
+    const long gf = udiv((x0 + 1) * G + W - 1, W) - 1;
+    const long gl = udiv((x1 + 1) * G + W - 1, W) - 1;
     // the parts go to the contributors whose range ends inside the tile: the last
     // contributor's range usually goes on into the next tiles (the tile is its first,
     // stored long before), so it takes a part only when its range ends with the tile
