@@ -137,6 +137,13 @@ __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t r, int off, void* 
 __device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t r, int off, void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
 }
+// The same with the offset split into a per-lane part (one VGPR shared by a run of
+// copies) and a uniform part in the instruction's scalar offset: no address arithmetic
+// on the VALU per copy.
+template <int AUX = 0>
+__device__ __forceinline__ void copy16s(__amdgpu_buffer_rsrc_t r, int voff, int soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, AUX);
+}
 
 // bf16 rounding (nearest, ties to even) by the hardware's packed conversion
 // (v_cvt_pk_bf16_f32): bit-identical to the software rounding on finite values, ties,
@@ -355,10 +362,10 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
     asm volatile("" : "+s"(ua), "+s"(da), "+s"(ub), "+s"(db));
 #pragma unroll
     for (int it = 0; it < C::A_DMA; ++it, ua += 8 * K)
-      copy16<0>(ra, lane_off + ua, st + da + it * 1024);
+      copy16s<0>(ra, lane_off, ua, st + da + it * 1024);
 #pragma unroll
     for (int it = 0; it < C::B_DMA; ++it, ub += 8 * K)
-      copy16<C::B_NT ? 2 : 0>(rb, lane_off + ub, st + db + it * 1024);
+      copy16s<C::B_NT ? 2 : 0>(rb, lane_off, ub, st + db + it * 1024);
   } else {
 #pragma unroll
     for (int it = 0; it < C::A_DMA; ++it) {
