@@ -150,11 +150,11 @@ def main():
                                             "pages_gbs", "roofline", "per_shape")}
             | {"workload": WORKLOAD_TEXT[n]}
             for n in names[1:]}
-    if "masked_decode_latency_us" in r:
-        line["masked_decode_latency_us"] = r["masked_decode_latency_us"]
-    elif len(names) > 1 and "masked_decode_latency_us" in results.get("masked", {}):
-        line["workloads"]["masked"]["masked_decode_latency_us"] = \
-            results["masked"]["masked_decode_latency_us"]
+    for key in ("masked_decode_latency_us", "masked_step_latency_us"):
+        if key in r:
+            line[key] = r[key]
+        elif len(names) > 1 and key in results.get("masked", {}):
+            line["workloads"]["masked"][key] = results["masked"][key]
     if args.detail:
         with open(args.detail, "w") as f:
             json.dump(dict(line=line, detail={n: results[n]["detail"] for n in names}), f,
@@ -341,6 +341,8 @@ def measure(name, args, torch, np, dg, I, dev, headline=False):
     if name == "masked":
         out["masked_decode_latency_us"] = masked_graph_latency(torch, np, dev, problems, calls,
                                                                args.steps)
+        out["masked_step_latency_us"] = masked_step_latency(torch, np, dev, problems, calls,
+                                                            args.steps)
     if headline:
         out["sclk_mhz"] = None if args.no_sclk else sclk_while_running(torch, calls[dom], 2.0)
         if not args.no_cpu_baseline:
@@ -437,6 +439,46 @@ def masked_graph_latency(torch, np, dev, problems, calls, steps):
         out.append(res)
     torch.cuda.synchronize()
     return out
+
+
+def masked_step_latency(torch, np, dev, problems, calls, steps):
+    """A decode step as a serving loop runs it: fresh masked_m for every call of the
+    workload (device copies from a table of seeded draws), all the calls, then a host
+    synchronisation (the host needs the step's results before the next).  The calls run
+    either as eager launches or as one replay of a HIP graph that holds all of them.
+    Returns {"eager": us/step, "graph": us/step, "calls": n}, wall clock over `steps`."""
+    mms = [c["masked_m"] for c in calls]
+    saved = [m.clone() for m in mms]
+    tables = [torch.from_numpy(np.random.default_rng(p.seed + 2000).integers(
+        0, p.M + 1, (16, p.G)).astype(np.int32)).to(dev) for p in problems]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.graph(graph, stream=side):
+        for c in calls:
+            c["fn"]()
+    torch.cuda.synchronize()
+    res = {"calls": len(calls)}
+    for use_graph in (False, True):
+        def step(i):
+            for m, t in zip(mms, tables):
+                m.copy_(t[i % 16])
+            if use_graph:
+                graph.replay()
+            else:
+                for c in calls:
+                    c["fn"]()
+            torch.cuda.synchronize()
+        for i in range(3):
+            step(i)
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        res["graph" if use_graph else "eager"] = round((time.perf_counter() - t0) * 1e6 / steps, 1)
+    for m, v in zip(mms, saved):
+        m.copy_(v)
+    torch.cuda.synchronize()
+    return res
 
 
 def bench_quant(args, torch, np, dg, I, dev):
