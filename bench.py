@@ -575,8 +575,14 @@ _ROOT = os.path.dirname(os.path.abspath(__file__))
 _KERNEL_SOURCES = ["moe_grouped_gemm_lhs_amd/csrc/dg_kernels.hip",
                    "moe_grouped_gemm_lhs_amd/csrc/dg_internal.h",
                    "moe_grouped_gemm_lhs_amd/csrc/dg_host.cpp"]
-_TRAFFIC_FILES = {("dense_128x128_stream_4w", "dense_128x7168x16384"):
-                  "profiles/decode_stream_kernel_hbm_traffic.txt"}
+_TRAFFIC_FILES = {
+    ("dense_128x128_stream_4w", "dense_128x7168x16384"):
+        "profiles/decode_dense_128x128_stream_4w_hbm_traffic.txt",
+    ("dense_256x224", "dense_4096x7168x16384"): "profiles/prefill_dense_256x224_hbm_traffic.txt",
+    ("contig_256x256", "contig_8xrand_4096x7168"):
+        "profiles/contiguous_contig_256x256_hbm_traffic.txt",
+    ("masked_128x128", "masked_4x256_4096x7168"): "profiles/masked_masked_128x128_hbm_traffic.txt",
+}
 
 
 def _profiled_traffic(instance, shape):
