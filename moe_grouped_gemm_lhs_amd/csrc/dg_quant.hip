@@ -73,8 +73,11 @@ constexpr float kMinReciprocalScale = 0x1p-64f;
 // (amax below FMAX * 2^-64: tiny and subnormal inputs, where 1/scale overflows or the
 // residual underflows) take the IEEE division instead; there a scale that underflowed to
 // zero gives +-inf (saturated below) and 0/0 a zero with the sign of x.
+// TINY: some lane of the wave holds such a block (decided once per wave by the caller,
+// so that the usual case carries no division at all).
+template <bool TINY>
 __device__ __forceinline__ float div_by_scale(float x, float scale, float r) {
-  if (scale >= kMinReciprocalScale) {
+  if (!TINY || scale >= kMinReciprocalScale) {
     const float y = x * r;
     const float e = __builtin_fmaf(-y, scale, x);
     return __builtin_copysignf(__builtin_fmaf(e, r, y), x);
@@ -85,12 +88,12 @@ __device__ __forceinline__ float div_by_scale(float x, float scale, float r) {
 
 // Four codes: the quotients saturated to +-FMAX, then converted by the hardware's
 // round-to-nearest-even fp8 conversion (OCP E4M3 / E5M2 on gfx950).
-template <int FMT>
+template <int FMT, bool TINY>
 __device__ __forceinline__ uint32_t pack4(const float* x, float scale, float r) {
   const float m = fp8_max<FMT>();
   float q[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(div_by_scale(x[i], scale, r), -m), m);
+  for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(div_by_scale<TINY>(x[i], scale, r), -m), m);
   int v;
   if (FMT == kFmtE5M2) {
     v = __builtin_amdgcn_cvt_pk_bf8_f32(q[0], q[1], 0, false);
@@ -103,13 +106,22 @@ __device__ __forceinline__ uint32_t pack4(const float* x, float scale, float r) 
 }
 
 // E codes of one 16-byte load, stored with one 8- or 4-byte store.
+template <int FMT, bool BF16, bool TINY>
+__device__ __forceinline__ void store_codes_as(uint8_t* Q, int64_t i, const float* x, float scale,
+                                               float r) {
+  if (BF16)
+    *(uint2*)(Q + i) =
+        make_uint2(pack4<FMT, TINY>(x, scale, r), pack4<FMT, TINY>(x + 4, scale, r));
+  else
+    *(uint32_t*)(Q + i) = pack4<FMT, TINY>(x, scale, r);
+}
 template <int FMT, bool BF16>
 __device__ __forceinline__ void store_codes(uint8_t* Q, int64_t i, const float* x, float scale,
                                             float r) {
-  if (BF16)
-    *(uint2*)(Q + i) = make_uint2(pack4<FMT>(x, scale, r), pack4<FMT>(x + 4, scale, r));
+  if (__builtin_amdgcn_ballot_w64(scale < kMinReciprocalScale) == 0)
+    store_codes_as<FMT, BF16, false>(Q, i, x, scale, r);
   else
-    *(uint32_t*)(Q + i) = pack4<FMT>(x, scale, r);
+    store_codes_as<FMT, BF16, true>(Q, i, x, scale, r);
 }
 
 // 1x128 blocks: LPB = 128/E lanes per block (16 for bf16, 32 for fp32), each with one
