@@ -580,7 +580,9 @@ _TRAFFIC_FILES = {
         "profiles/decode_dense_128x128_stream_4w_hbm_traffic.txt",
     ("dense_256x224", "dense_4096x7168x16384"): "profiles/prefill_dense_256x224_hbm_traffic.txt",
     ("contig_256x256", "contig_8xrand_4096x7168"):
-        "profiles/contiguous_contig_256x256_hbm_traffic.txt",
+        "profiles/contiguous_contig_256x256_8xrand_hbm_traffic.txt",
+    ("contig_256x256", "contig_4x8192_4096x7168"):
+        "profiles/contiguous_contig_256x256_4x8192_hbm_traffic.txt",
     ("masked_128x128", "masked_4x256_4096x7168"): "profiles/masked_masked_128x128_hbm_traffic.txt",
 }
 
