@@ -243,7 +243,8 @@ def test_formats_every_form(a_fmt, b_fmt):
 def test_formats_every_instance(a_fmt, b_fmt, monkeypatch):
     """Each dense instance forced with E5M2 operands."""
     from moe_grouped_gemm_lhs_amd import binding as b
-    for name in ["dense_256x256", "dense_256x224", "dense_128x128", "dense_64x128_stream",
+    for name in ["dense_256x256", "dense_256x224", "dense_256x160", "dense_128x128",
+                 "dense_64x128_stream",
                  "dense_64x64_stream", "dense_128x128_stream", "dense_128x64_stream",
                  "dense_128x128_stream_4w", "dense_64x128_stream_4w"]:
         monkeypatch.setenv("DG_FORCE_INSTANCE", name)
@@ -251,6 +252,26 @@ def test_formats_every_instance(a_fmt, b_fmt, monkeypatch):
         assert b.dg_instance_name(0, M, 400, 512, 1) == name
         p = I.make_dense(M, 400, 512, seed=64, a_fmt=a_fmt, b_fmt=b_fmt)
         check_full(p, f"dense forced {name} {a_fmt}x{b_fmt}")
+    monkeypatch.delenv("DG_FORCE_INSTANCE")
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", FMT_PAIRS)
+def test_formats_every_grouped_instance(a_fmt, b_fmt, monkeypatch):
+    """Each contiguous and masked instance forced with E5M2 operands (the split-K masked
+    instances too, on groups of several 128-row tiles)."""
+    from moe_grouped_gemm_lhs_amd import binding as b
+    fm = dict(a_fmt=a_fmt, b_fmt=b_fmt)
+    for name in ["contig_256x256", "contig_256x224", "contig_128x128"]:
+        monkeypatch.setenv("DG_FORCE_INSTANCE", name)
+        p = I.make_contiguous([256, 128, 384], 400, 384, seed=65, **fm)
+        assert b.dg_instance_name(1, p.rows, p.N, p.K, p.G) == name
+        check_full(p, f"contiguous forced {name} {a_fmt}x{b_fmt}")
+    for name in ["masked_256x256", "masked_128x128", "masked_64x128", "masked_128x128_stream",
+                 "masked_128x64_stream"]:
+        monkeypatch.setenv("DG_FORCE_INSTANCE", name)
+        p = I.make_masked(3, 200, 400, 384, seed=66, masked_m=[200, 37, 130], **fm)
+        assert b.dg_instance_name(2, 200, 400, 384, 3) == name
+        check_full(p, f"masked forced {name} {a_fmt}x{b_fmt}")
     monkeypatch.delenv("DG_FORCE_INSTANCE")
 
 
