@@ -220,6 +220,14 @@ dg_status run(int kind, int fa, int fb, GemmArgs& a, void* workspace, size_t wor
     if (!workspace || workspace_bytes < ws || !aligned(workspace, 16)) return DG_ERR_WORKSPACE;
     a.arrivals = (int*)workspace;
     a.partial = (float*)((uint8_t*)workspace + dg::kArrivalBytes);
+    // DG_HELPER_POLLS=<n>: a smaller bound on the owners' polls, so that tests can make
+    // every part of a shared tile fall to its last contributor
+    a.helper_polls = dg::kHelperPolls;
+    if (const char* e = getenv("DG_HELPER_POLLS")) {
+      char* end = nullptr;
+      const long v = strtol(e, &end, 10);
+      if (end != e && v >= 0 && v < dg::kHelperPolls) a.helper_polls = (int)v;
+    }
   }
   if (in->mode == dg::kModeStream && !a.partial)
     return DG_ERR_WORKSPACE;

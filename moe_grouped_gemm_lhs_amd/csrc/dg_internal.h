@@ -19,7 +19,8 @@ constexpr int kStreamGrid = 256;
 constexpr int kArrivalBytes = kStreamGrid * 8 * 8;
 // Bound on a contributor's polls for the other partials of its part of a shared tile
 // (about a microsecond each); when it runs out the contributor leaves the part to the
-// last contributor to arrive, which never waits.
+// last contributor to arrive, which never waits.  The host may lower it per call
+// (DG_HELPER_POLLS, for tests of that hand-over).
 constexpr int kHelperPolls = 2000;
 
 // Workgroups of a dense stream-K launch over `tiles` output tiles of `nkb` K blocks on
@@ -56,6 +57,7 @@ struct GemmArgs {
   const int32_t* masked_m;    // masked only
   float* partial;             // stream-K fp32 partial tiles (workspace), or nullptr
   int* arrivals;              // stream-K arrival counters per shared tile (workspace)
+  int helper_polls;           // stream-K: bound on an owner's polls (kHelperPolls)
   int rows;                   // dense M, contiguous M_total, masked cap
   int N, K, G;
   int nkb;                    // K / 128

@@ -1379,8 +1379,9 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   for (int k = 0; k < 4; ++k) {
     if (k == 2) {
       // this wave's partial stores are complete before its arrival is counted: a wave
-      // that polled has used loads issued after them (vmcnt retires in issue order)
-      if (!polled) wait_vmcnt<0>();
+      // that polled has used loads issued after them (vmcnt retires in issue order); with
+      // a zero poll bound nothing was loaded
+      if (!polled || p.helper_polls == 0) wait_vmcnt<0>();
       unsigned long long before[2] = {0ull, 0ull};
 #pragma unroll
       for (int sg = 0; sg < 2; ++sg) {
@@ -1398,7 +1399,9 @@ gemm_fp8_stream_kernel(GemmArgs p) {
         const int lo = __builtin_amdgcn_readlane((int)before[sg], 0);
         if (hi == nv[sg] - 1) {                 // the last to arrive
           const int mine_done = (okmask >> sg) & 1 ? 1 << cv[sg] : 0;
-          const int left = ((1 << pv[sg]) - 1) & ~(lo | mine_done);
+          // every part (P can be 32: no 1 << 32 on a 32-bit int)
+          const unsigned all = pv[sg] >= 32 ? ~0u : (1u << pv[sg]) - 1u;
+          const int left = (int)(all & ~(unsigned)(lo | mine_done));
           if (sg) left1 = left; else left0 = left;
           if (lane == 0)
             __hip_atomic_store((unsigned long long*)p.arrivals + gfv[sg] * C::W + wave, 0ull,
@@ -1416,8 +1419,10 @@ gemm_fp8_stream_kernel(GemmArgs p) {
     const int row0 = sg ? seg_row0[1] : seg_row0[0];
     const int rows = sg ? seg_rows[1] : seg_rows[0];
     const int n0 = sg ? seg_n0[1] : seg_n0[0];
+    // an owner polls at most helper_polls times; the last arrival's partials are all
+    // stored, so its leftover parts never wait
     if (reduce_parts<C, false>(mask, P, n, gf, fs, part_rsrc, p, row0, rows, n0, wave, wm, wn,
-                               lane, kHelperPolls)) {
+                               lane, k < 2 ? p.helper_polls : kHelperPolls)) {
       reduce_parts<C, true>(mask, P, n, gf, fs, part_rsrc, p, 0, 0, 0, wave, wm, wn, lane, 0);
       if (k < 2) okmask |= 1 << sg;
     }

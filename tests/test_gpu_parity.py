@@ -175,6 +175,43 @@ def test_stream_k_shared_tiles(M, N, K, monkeypatch):
     monkeypatch.delenv("DG_FORCE_INSTANCE")
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 64, 128 * 200), (128, 200, 16384), (100, 1000, 128 * 40)])
+def test_stream_k_owners_give_up(M, N, K, monkeypatch):
+    """The hand-over of a shared tile's parts: with the owners' poll bound forced to 0 or 1
+    (DG_HELPER_POLLS, set from the host) owners give up at once and the last contributor
+    to arrive reduces what is left.  Every part is summed in the same order whoever
+    reduces it, so the output is bit-identical to the default run; the workspace is left
+    zero filled."""
+    from moe_grouped_gemm_lhs_amd import binding as b
+    p = I.make_dense(M, N, K, seed=M + N + K // 128 + 1)
+    A, sA, B, sB = gu.device_operands(p)
+    c_ref = gu.oracle_full(p)
+    written = np.ones((M, N), bool)
+    for name in ["dense_64x128_stream", "dense_128x128_stream_4w", "dense_128x64_stream"]:
+        if M > int(name.split("_")[1].split("x")[0]):
+            continue
+        monkeypatch.setenv("DG_FORCE_INSTANCE", name)
+        ws = torch.zeros(b.dg_workspace_bytes(0, M, N, K, 1), dtype=torch.uint8, device=gu.DEV)
+        monkeypatch.delenv("DG_HELPER_POLLS", raising=False)
+        gu.say(f"[case] stream {name} {M}x{N}x{K} default poll bound")
+        base = gu.run_gpu(p, ops=(A, sA, B, sB), workspace=ws)
+        assert_within_tolerance(base, c_ref, written, f"{name} {M}x{N}x{K}")
+        for polls in ("0", "1"):
+            monkeypatch.setenv("DG_HELPER_POLLS", polls)
+            gu.say(f"[case] stream {name} {M}x{N}x{K} poll bound {polls}")
+            c_gpu = gu.run_gpu(p, ops=(A, sA, B, sB), workspace=ws)
+            diff = np.argwhere(c_gpu != base)
+            if diff.size:
+                gu.say(f"[diag] {len(diff)} elements differ, first {diff[:4].tolist()}: "
+                       f"{c_gpu[tuple(diff[0])]:#06x} vs {base[tuple(diff[0])]:#06x}; "
+                       f"workspace zero: {not ws.cpu().numpy().any()}")
+            assert_within_tolerance(c_gpu, c_ref, written, f"{name} poll bound {polls}")
+            assert np.array_equal(c_gpu, base), f"{name}: poll bound {polls} changed the output"
+            assert not ws.cpu().numpy().any(), f"{name}: workspace not left zero filled"
+        monkeypatch.delenv("DG_HELPER_POLLS")
+    monkeypatch.delenv("DG_FORCE_INSTANCE")
+
+
 MASKED_STREAM_INSTANCES = ["masked_128x128_stream", "masked_128x64_stream"]
 
 
