@@ -55,7 +55,7 @@ def run_gpu(p, c_init_bits=None, group_idx=None, masked_m=None, ops=None, worksp
         mm = masked_m if masked_m is not None else p.masked_m
         Cv = C.view(p.G, p.M, p.N)
         dg.dg_grouped_gemm_fp8_masked(A, sA, B, sB, torch.from_numpy(np.asarray(mm, np.int32)).to(DEV), Cv,
-                                      **fm)
+                                      workspace=workspace, **fm)
     torch.cuda.synchronize()
     return C.view(torch.int16).cpu().numpy().view(np.uint16).reshape(out_shape(p))
 

@@ -215,6 +215,32 @@ def test_stream_k_owners_give_up(M, N, K, monkeypatch):
 MASKED_STREAM_INSTANCES = ["masked_128x128_stream", "masked_128x64_stream"]
 
 
+@pytest.mark.parametrize("G,cap,N,K,mm", [(2, 128, 130, 128 * 60, [128, 70]),
+                                         (4, 512, 256, 2048, [512, 0, 300, 129])])
+def test_masked_stream_k_owners_give_up(G, cap, N, K, mm, monkeypatch):
+    """The masked split-K instances with the owners' poll bound forced to 0: every part of
+    every shared tile falls to its last contributor; the output is bit-identical to the
+    default run and the workspace is left zero filled."""
+    from moe_grouped_gemm_lhs_amd import binding as b
+    p = I.make_masked(G, cap, N, K, seed=G * 11 + cap, masked_m=mm)
+    ops = gu.device_operands(p)
+    for name in MASKED_STREAM_INSTANCES:
+        monkeypatch.setenv("DG_FORCE_INSTANCE", name)
+        ws = torch.zeros(b.dg_workspace_bytes(2, cap, N, K, G), dtype=torch.uint8, device=gu.DEV)
+        monkeypatch.delenv("DG_HELPER_POLLS", raising=False)
+        gu.say(f"[case] {name} G={G} cap={cap} default poll bound")
+        base = gu.run_gpu(p, ops=ops, workspace=ws)
+        monkeypatch.setenv("DG_HELPER_POLLS", "0")
+        gu.say(f"[case] {name} G={G} cap={cap} poll bound 0")
+        c_gpu = gu.run_gpu(p, ops=ops, workspace=ws)
+        assert np.array_equal(c_gpu, base), f"{name}: poll bound 0 changed the output"
+        assert not ws.cpu().numpy().any(), f"{name}: workspace not left zero filled"
+        monkeypatch.delenv("DG_HELPER_POLLS")
+    monkeypatch.delenv("DG_FORCE_INSTANCE")
+
+
+
+
 @pytest.mark.parametrize("G,cap,N,K,mm", [
     (3, 200, 400, 384, [200, 37, 0]),                      # ragged rows, an empty group
     (6, 96, 300, 512, [0, 96, 1, 95, -5, 103]),            # counts outside [0, cap]
