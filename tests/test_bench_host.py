@@ -42,3 +42,35 @@ def test_pages_gbs_convention_reproduces_the_tables():
     assert abs(gbs(c, 4 * 8192, 1297) - 418) < 3
     m = P(); m.kind, m.G, m.M, m.N, m.K = "masked", 4, 256, 4096, 7168
     assert abs(gbs(m, 4 * 256, 932) - 2064) < 3
+
+
+def test_traffic_summaries_match_the_kernel_sources():
+    """Every dominant kernel the bench maps to a committed HBM traffic summary has one, it
+    parses, and its source hash matches the kernel sources as they stand (bench.py reports
+    `traffic` only then); the algorithmic bytes recorded with it are the bench's own."""
+    for (inst, shape), rel in bench._TRAFFIC_FILES.items():
+        path = os.path.join(ROOT, rel)
+        assert os.path.exists(path), rel
+        t = bench._profiled_traffic(inst, shape)
+        assert t is not None and t > 0, f"{rel}: stale or unparsable"
+        fields = dict(l.split(":", 1) for l in open(path) if ":" in l)
+        assert inst in fields["kernel"] and shape in fields["kernel"], rel
+        assert int(fields["traffic_bytes_per_launch"].strip()) == t
+
+
+def test_traffic_is_withheld_when_the_sources_change(tmp_path, monkeypatch):
+    """A kernel source that no longer hashes to the recorded value switches `traffic` off."""
+    (inst, shape), rel = next(iter(bench._TRAFFIC_FILES.items()))
+    srcs = []
+    for s in bench._KERNEL_SOURCES:
+        dst = tmp_path / os.path.basename(s)
+        dst.write_bytes(open(os.path.join(ROOT, s), "rb").read())
+        srcs.append(str(dst))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / rel).write_text(open(os.path.join(ROOT, rel)).read())
+    monkeypatch.setattr(bench, "_ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "_KERNEL_SOURCES", srcs)
+    assert bench._profiled_traffic(inst, shape) is not None
+    with open(srcs[0], "ab") as f:
+        f.write(b"\n// changed\n")
+    assert bench._profiled_traffic(inst, shape) is None
