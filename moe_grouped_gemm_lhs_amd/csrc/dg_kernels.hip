@@ -125,6 +125,7 @@ __device__ __forceinline__ void wait_copies_pf(int wave, int ahead, int epis) {
 }
 template <class C, int NST>
 __device__ __forceinline__ void wait_copies_epi(int wave, int ahead, int epis) {
+  if (wave < 0) return;   // a compute-only wave: it has no copies to wait for
   if (wave < C::S_WAVES)
     wait_copies_pf<C, NST, C::PER_STAGE>(wave, ahead, epis);
   else if (wave < C::CW)
@@ -217,20 +218,26 @@ __device__ __forceinline__ void stage_barrier() {
 // Compile-time shape of one kernel instance.
 // B_NT: B blocks are read by exactly one workgroup (decode shapes), so they are loaded
 // non-temporal.  FMT_A / FMT_B: operand formats (0: E4M3, 1: E5M2).
-// CW_: how many waves issue the stage copies (0: all).  A wave's copies queue in the CU's
+// CW_: how many waves issue the stage copies (0: all).
+// XW_: copy-only waves after the compute waves (0: none).  With XW_ > 0 the XW_ extra
+// waves issue every copy and never compute, and the compute waves issue none: a wave's
+// MFMAs then never queue behind its own copies in the CU's address unit, which all
+// copying waves share.  A wave's copies queue in the CU's
 // address unit behind the other waves' (one 1 KB copy per 16 clocks at most), and a wave
 // cannot start its MFMAs until its own copies are issued; with two waves per SIMD, giving
 // all copies to the first wave of each SIMD lets the second start computing at once.
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, bool B_NT_ = false,
-          int FMT_A_ = 0, int FMT_B_ = 0, int CW_ = 0, int PFD_ = 0>
+          int FMT_A_ = 0, int FMT_B_ = 0, int CW_ = 0, int PFD_ = 0, int XW_ = 0>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int STAGES = STAGES_;
   static constexpr bool B_NT = B_NT_;
   static constexpr int FMT_A = FMT_A_, FMT_B = FMT_B_;
-  static constexpr int W = WAVES_M * WAVES_N;
-  static constexpr int CW = CW_ ? CW_ : W;      // copy waves: 0 .. CW-1
-  static constexpr int NT = 64 * W;
+  static constexpr int W = WAVES_M * WAVES_N;    // compute waves: 0 .. W-1
+  static constexpr int XW = XW_;
+  static constexpr int CW = XW_ ? XW_ : (CW_ ? CW_ : W);   // copy waves: CW0 .. CW0+CW-1
+  static constexpr int CW0 = XW_ ? W : 0;
+  static constexpr int NT = 64 * (W + XW_);
   static constexpr int WM = BM / WAVES_M;       // rows per wave
   static constexpr int WN = BN / WAVES_N;       // columns per wave
   static constexpr int TI = WM / 16;            // 16-row sub-tiles per wave
@@ -349,6 +356,7 @@ struct TileCtx {
   int n0;
   int nb_first;  // sB block of column n0
   int wave, lane, wm, wn, q, l16;
+  int cw;        // index among the copy waves (negative: a wave that issues no copies)
 };
 
 // Direct-to-LDS copy of K block kb of the tile into stage `st`.  The copies go through
@@ -362,7 +370,7 @@ struct TileCtx {
 template <class C, bool FRESH = false>
 __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const TileCtx& c, int kb,
                                             uint8_t* dump = nullptr) {
-  if (c.wave >= C::CW) return;             // not a copy wave
+  if (c.cw < 0 || c.cw >= C::CW) return;   // not a copy wave
   const int sub = c.lane >> 3;             // row inside the 8-row block
   const int ch = (c.lane & 7) ^ sub;       // global chunk for this lane's slot
   const int K = c.K;
@@ -374,8 +382,8 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
     // The uniform parts are advanced copy by copy from starting values the compiler
     // cannot see through, so it keeps no per-copy offsets or LDS addresses live from
     // one call to the next (one per-lane term and a few scalars per call instead).
-    int ua = c.wave * (C::A_DMA * 8) * K + kb * kBlockK, da = c.wave * C::A_DMA * 1024;
-    int ub = c.wave * (C::B_DMA * 8) * K + kb * kBlockK, db = C::A_BYTES + c.wave * C::B_DMA * 1024;
+    int ua = c.cw * (C::A_DMA * 8) * K + kb * kBlockK, da = c.cw * C::A_DMA * 1024;
+    int ub = c.cw * (C::B_DMA * 8) * K + kb * kBlockK, db = C::A_BYTES + c.cw * C::B_DMA * 1024;
     asm volatile("" : "+s"(ua), "+s"(da), "+s"(ub), "+s"(db));
 #pragma unroll
     for (int it = 0; it < C::A_DMA; ++it, ua += 8 * K)
@@ -386,29 +394,31 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
   } else {
 #pragma unroll
     for (int it = 0; it < C::A_DMA; ++it) {
-      const int cb = c.wave * C::A_DMA + it;
+      const int cb = c.cw * C::A_DMA + it;
       copy16<0>(ra, lane_off + (cb * 8 * K + kb * kBlockK), st + cb * 1024);
     }
 #pragma unroll
     for (int it = 0; it < C::B_DMA; ++it) {
-      const int cb = c.wave * C::B_DMA + it;
+      const int cb = c.cw * C::B_DMA + it;
       copy16<C::B_NT ? 2 : 0>(rb, lane_off + (cb * 8 * K + kb * kBlockK),
                               st + C::A_BYTES + cb * 1024);
     }
   }
-  if (c.wave < C::S_WAVES) {
+  if (c.cw < C::S_WAVES) {
     // slot s < BM: sA of row s; slot BM + j: sB of column block nb_first + j (the slots
     // after the tile's NBV blocks, and any padding slots, are filled but never read)
     const __amdgpu_buffer_rsrc_t rsa =
         buffer_over(c.sA + (size_t)c.a_row0 * c.nkb, c.rows * c.nkb * 4);
-    const __amdgpu_buffer_rsrc_t rsb =
-        buffer_over(c.sBg + (size_t)c.nb_first * c.nkb, (c.nnb - c.nb_first) * c.nkb * 4);
+    // sB: only the NBV blocks the tile can touch, so that the other lanes of its copy
+    // (one sB row each, a line apiece) fetch nothing
+    const __amdgpu_buffer_rsrc_t rsb = buffer_over(
+        c.sBg + (size_t)c.nb_first * c.nkb, min(C::NBV, c.nnb - c.nb_first) * c.nkb * 4);
     int sl = c.lane;
     if (FRESH) asm volatile("" : "+v"(sl));
     const int s_off = sl * c.nkb * 4 + kb * 4;
 #pragma unroll
     for (int it = 0; it < C::S_PER; ++it) {
-      const int slot = c.wave * C::S_PER + it;
+      const int slot = c.cw * C::S_PER + it;
       uint8_t* dst = st + C::A_BYTES + C::B_BYTES + slot * 256;
       if (slot * 64 < C::BM)
         copy4(rsa, s_off + slot * 64 * c.nkb * 4, dst);
@@ -416,7 +426,7 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
         copy4(rsb, s_off + (slot * 64 - C::BM) * c.nkb * 4, dst);
     }
   }
-  if (C::PF_WAVES > 0 && c.wave < C::PF_WAVES) {
+  if (C::PF_WAVES > 0 && c.cw < C::PF_WAVES) {
     // The lines of K block kb + PFD that this workgroup brings into the L2 for its XCD.
     // The 32 workgroups of an XCD run 32 consecutive tiles, 4 row tiles by 8 column tiles
     // (4-row-tile bands, column-major), so each A row tile is read by 8 of them and each
@@ -428,10 +438,10 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
     const int kp = kb + C::PFD;
     const int tn = c.n0 / C::BN, tm = c.a_row0 / C::BM;
     int row = -1;
-    if (c.wave == 0 && c.lane < C::BM / 8) row = (tn & 7) * (C::BM / 8) + c.lane;
-    if (c.wave == 1 && c.lane < C::BN / 4) row = (tm & 3) * (C::BN / 4) + c.lane;
+    if (c.cw == 0 && c.lane < C::BM / 8) row = (tn & 7) * (C::BM / 8) + c.lane;
+    if (c.cw == 1 && c.lane < C::BN / 4) row = (tm & 3) * (C::BN / 4) + c.lane;
     const int off = kp < c.nkb && row >= 0 ? row * K + kp * kBlockK : 0x7FFFFFF0;
-    copy4(c.wave == 1 ? rb : ra, off, dump);
+    copy4(c.cw == 1 ? rb : ra, off, dump);
   }
 }
 
@@ -881,8 +891,13 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
   constexpr bool DIRECT = KIND != kContiguous;
   constexpr int NST = DIRECT ? direct_stores<C>() : E::NST;
   static_assert((STAGES - 2) * (C::PER_STAGE + 1) + 1 + (STAGES - 1) * NST < 64, "vmcnt range");
+  // copy-only waves: they store nothing, so their waits never count epilogue stores
+  constexpr bool SPEC = C::XW > 0;
+  static_assert(!SPEC || DIRECT, "copy-only waves with the register epilogue only");
   const int nkb = p.nkb;
   const int wave = c.wave;
+  const int cw = c.cw;
+  const bool computes = !SPEC || wave < C::W;
 
   // w: the item being multiplied; wx: the next one, whose first K blocks are copied
   // during w's last steps (when every item has at least STAGES-1 K blocks; otherwise
@@ -912,7 +927,7 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
   int sn = 0, sc = 0;
   for (;;) {
     const bool more = cross && wx.t < nwork;
-    const int epi_n = stored ? 1 : 0;
+    const int epi_n = stored && !SPEC ? 1 : 0;
     if (fill) {
       for (int f = 0; f < STAGES - 1 && f < nkb; ++f) {
         issue_stage<C, true>(cp + sn * C::STAGE_BYTES, c, f, cp + STAGES * C::STAGE_BYTES);
@@ -922,27 +937,27 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
     int kb = 0;
     // copies of this item's later blocks
     for (; kb + STAGES - 1 < nkb; ++kb) {
-      wait_copies_epi<C, NST>(wave, STAGES - 2, kb <= STAGES - 2 ? epi_n : 0);
+      wait_copies_epi<C, NST>(cw, STAGES - 2, kb <= STAGES - 2 ? epi_n : 0);
       stage_barrier();
       issue_stage<C, true>(cp + sn * C::STAGE_BYTES, c, kb + STAGES - 1,
                            cp + STAGES * C::STAGE_BYTES);
       sn = sn + 1 == STAGES ? 0 : sn + 1;
-      compute_stage<C>(rd + sc * C::STAGE_BYTES, c, acc);
+      if (computes) compute_stage<C>(rd + sc * C::STAGE_BYTES, c, acc);
       sc = sc + 1 == STAGES ? 0 : sc + 1;
     }
     // the last STAGES-1 steps: copies of the next item's first blocks, then the epilogue
     bool fast = false;
     for (; kb < nkb; ++kb) {
-      wait_copies_epi<C, NST>(wave, more ? STAGES - 2 : min(STAGES - 2, nkb - 1 - kb),
-                                 kb <= STAGES - 2 ? epi_n : 0);
+      wait_copies_epi<C, NST>(cw, more ? STAGES - 2 : min(STAGES - 2, nkb - 1 - kb),
+                              kb <= STAGES - 2 ? epi_n : 0);
       stage_barrier();
       if (more) {
         issue_stage<C, true>(cp + sn * C::STAGE_BYTES, cx, kb + STAGES - 1 - nkb,
                              cp + STAGES * C::STAGE_BYTES);
         sn = sn + 1 == STAGES ? 0 : sn + 1;
       }
-      compute_stage<C>(rd + sc * C::STAGE_BYTES, c, acc);
-      if (kb == nkb - 1) {
+      if (computes) compute_stage<C>(rd + sc * C::STAGE_BYTES, c, acc);
+      if (kb == nkb - 1 && computes) {
         TileOut o;
         o.a_row0 = c.a_row0;
         o.rows = c.rows;
@@ -995,6 +1010,7 @@ gemm_fp8_kernel(GemmArgs p) {
   c.N = p.N;
   c.lane = tid & 63;
   c.wave = uniform(tid >> 6);
+  c.cw = c.wave - C::CW0;
   c.wm = c.wave / C::WAVES_N;
   c.wn = c.wave - c.wm * C::WAVES_N;
   c.q = c.lane >> 4;
@@ -1257,6 +1273,7 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   constexpr int FRAG_FLOATS = 64 * 4;                        // one 16x16 fp32 sub-tile
   constexpr int WAVE_SLOT = TI * TJ * FRAG_FLOATS;           // one wave's partial
   static_assert(C::W <= 8, "the workspace holds one arrival record per wave, 8 per tile");
+  static_assert(C::XW == 0, "every wave of the stream kernel computes");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * C::STAGE_BYTES];
 
   const int tid = threadIdx.x;
@@ -1297,6 +1314,7 @@ gemm_fp8_stream_kernel(GemmArgs p) {
   cn.a_row0 = 0;
   cn.rows = p.rows;
   cn.wave = wave;
+  cn.cw = wave;
   cn.lane = lane;
   cn.wm = wm;
   cn.wn = wn;
@@ -1504,6 +1522,8 @@ template <int FA, int FB> using Big160 = Cfg<256, 160, 4, 2, 2, false, FA, FB, 4
 template <int FA, int FB> using BigC = Cfg<256, 256, 4, 2, 2, false, FA, FB, 4, 2>;
 template <int FA, int FB> using Big224C = Cfg<256, 224, 4, 2, 2, false, FA, FB>;
 template <int FA, int FB> using Mid = Cfg<128, 128, 2, 2, 3, false, FA, FB>;     // 4 waves, 64x64 each
+// the same with four copy-only waves (register epilogue forms: dense and masked)
+template <int FA, int FB> using MidS = Cfg<128, 128, 2, 2, 3, false, FA, FB, 0, 0, 4>;
 template <int FA, int FB> using Small = Cfg<64, 128, 1, 4, 4, false, FA, FB>;    // 4 waves, 64x32 each
 // stream-K decode instances: 8 waves (a wave's direct-to-LDS copies are issue-bound, so
 // a workgroup needs eight of them to draw its share of HBM bandwidth), B non-temporal
@@ -1538,7 +1558,7 @@ static const Instance kInstances[] = {
     DG_INST("dense_256x256", kDense, Big),
     DG_INST("dense_256x224", kDense, Big224),
     DG_INST("dense_256x160", kDense, Big160),
-    DG_INST("dense_128x128", kDense, Mid),
+    DG_INST("dense_128x128", kDense, MidS),
     DG_STREAM("dense_64x128_stream", kDense, Str64),
     DG_STREAM("dense_64x64_stream", kDense, Str64n64),
     DG_STREAM("dense_128x128_stream", kDense, Str128),
@@ -1549,7 +1569,7 @@ static const Instance kInstances[] = {
     DG_INST("contig_256x224", kContiguous, Big224C),
     DG_INST("contig_128x128", kContiguous, Mid),
     DG_INST("masked_256x256", kMasked, Big),
-    DG_INST("masked_128x128", kMasked, Mid),
+    DG_INST("masked_128x128", kMasked, MidS),
     DG_INST("masked_64x128", kMasked, Small),
     DG_STREAM("masked_128x128_stream", kMasked, Str128),
     DG_STREAM("masked_128x64_stream", kMasked, Str128n64),
