@@ -263,7 +263,11 @@ struct Cfg {
   // waves 0 (A rows) and 1 (B rows)
   static constexpr int PFD = PFD_;
   static constexpr int PF_WAVES = PFD_ > 0 ? 2 : 0;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + (PFD_ > 0 ? 256 : 0);
+  // LDS after the stages: the prefetch scratch slot, then (contiguous form) two slots of
+  // the tile rows' group indices, one per work item in flight
+  static constexpr int PF_OFF = STAGES * STAGE_BYTES;
+  static constexpr int GI_OFF = PF_OFF + (PFD_ > 0 ? 256 : 0);
+  static constexpr int LDS_BYTES = GI_OFF + 2 * BM * 4;
   // every wave's columns fall inside one 128-column scale block
   static constexpr bool ONE_NB =
       (128 % WN == 0) && ((BN % 128 == 0) || (128 % BN == 0));
@@ -357,6 +361,7 @@ struct TileCtx {
   int nb_first;  // sB block of column n0
   int wave, lane, wm, wn, q, l16;
   int cw;        // index among the copy waves (negative: a wave that issues no copies)
+  int gslot;     // contiguous form: the LDS slot of this item's group indices
 };
 
 // Direct-to-LDS copy of K block kb of the tile into stage `st`.  The copies go through
@@ -367,10 +372,20 @@ struct TileCtx {
 // term, all in the range-checked vector offset.  FRESH (the tiled kernel, whose loops
 // keep more state live): the offsets are rebuilt at every call instead of kept in
 // registers across calls.
-template <class C, bool FRESH = false>
+template <class C, bool FRESH = false, bool GI = false>
 __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const TileCtx& c, int kb,
-                                            uint8_t* dump = nullptr) {
+                                            uint8_t* base = nullptr,
+                                            const int32_t* gidx = nullptr) {
   if (c.cw < 0 || c.cw >= C::CW) return;   // not a copy wave
+  if (GI && kb == 0 && c.cw == 0) {
+    // contiguous form, with the item's first K block: its rows' group indices into the
+    // item's LDS slot, for the epilogue's row checks (rows past the tile's valid ones
+    // read zeros; the epilogue never stores them)
+    const __amdgpu_buffer_rsrc_t rg = buffer_over(gidx + c.a_row0, c.rows * 4);
+    uint8_t* gl = base + C::GI_OFF + c.gslot * (C::BM * 4);
+#pragma unroll
+    for (int it = 0; it < C::BM / 64; ++it) copy4(rg, (it * 64 + c.lane) * 4, gl + it * 256);
+  }
   const int sub = c.lane >> 3;             // row inside the 8-row block
   const int ch = (c.lane & 7) ^ sub;       // global chunk for this lane's slot
   const int K = c.K;
@@ -441,7 +456,7 @@ __device__ __forceinline__ void issue_stage(uint8_t* __restrict__ st, const Tile
     if (c.cw == 0 && c.lane < C::BM / 8) row = (tn & 7) * (C::BM / 8) + c.lane;
     if (c.cw == 1 && c.lane < C::BN / 4) row = (tm & 3) * (C::BN / 4) + c.lane;
     const int off = kp < c.nkb && row >= 0 ? row * K + kp * kBlockK : 0x7FFFFFF0;
-    copy4(c.cw == 1 ? rb : ra, off, dump);
+    copy4(c.cw == 1 ? rb : ra, off, base + C::PF_OFF);
   }
 }
 
@@ -551,30 +566,7 @@ __device__ __forceinline__ void store_tile_bf16(const v4f (&acc)[C::TI][C::TJ], 
 }
 
 // ------------------------------------------------------------------------------------
-// The tiled kernel's LDS-staged epilogue (the contiguous form, whose row checks read the
-// group indices of whole rows; the other forms store from registers, below): a finished
-// tile leaves through the LDS stage its last K block was read from (the copies in flight fill the other stages).  In EP passes of RP
-// rows each (as many as one stage holds), the waves write their fragments of the pass's
-// rows there as bf16 rows padded by 16 bytes (the fragment writes spread over the banks),
-// then store whole rows, 16 bytes per lane, RPI rows per store instruction.
-template <class C>
-struct Epi {
-  static constexpr int ROW_BYTES = C::BN * 2 + 16;
-  static constexpr int CHUNKS = C::BN / 8;                  // 16-byte chunks per row
-  static constexpr int RPI = 64 / CHUNKS;                   // rows per store instruction
-  static constexpr int passes() {
-    int e = 1;
-    while ((C::BM / e) * ROW_BYTES > C::STAGE_BYTES) e *= 2;
-    return e;
-  }
-  static constexpr int EP = passes();
-  static constexpr int RP = C::BM / EP;
-  static constexpr int SPP = (RP + C::W * RPI - 1) / (C::W * RPI);  // stores per wave, pass
-  static constexpr int NST = EP * SPP;                      // stores per wave, tile
-  static_assert(RPI >= 1 && RP % 16 == 0 && C::BM % EP == 0, "epilogue rows");
-  static_assert((C::STAGES - 2) * C::PER_STAGE + (C::STAGES - 1) * NST < 64, "vmcnt range");
-};
-
+// The tiled kernel's epilogue.
 // Offset past every tile's output range: a buffer store there is dropped.
 constexpr int kPastTile = 0x7FFFFF00;
 
@@ -587,127 +579,27 @@ struct TileOut {
   int lead0, lead1;  // contiguous: group index of each 128-row block's first row
 };
 
-// Stores of one tile from LDS stage `st`.  Fast form (N a multiple of 8): every wave
-// issues exactly Epi::NST buffer stores, whatever the tile; a chunk outside the tile's
-// rows or columns, or in a row of another group, gets an offset past the buffer's range,
-// which the hardware drops.  Otherwise chunks are stored element by element where they
-// straddle N, and the wave waits for all of its memory operations at the end.  Returns
-// whether the fast form was used.
-template <int KIND, class C>
-__device__ __forceinline__ bool store_tile_staged(uint8_t* __restrict__ st,
-                                                  const v4f (&acc)[C::TI][C::TJ],
-                                                  const GemmArgs& p, const TileOut& o,
-                                                  int wave, int lane, int wm, int wn, int q,
-                                                  int l16) {
-  using E = Epi<C>;
-  static_assert(E::RP % C::WM == 0, "a wave's rows fall in one pass");
-  const int N = p.N;
-  const bool fast = (N & 7) == 0 && (long)C::BM * N * 2 < (long)kPastTile;
-  const __amdgpu_buffer_rsrc_t rc =
-      buffer_over(p.C + (size_t)o.a_row0 * N, fast ? o.rows * N * 2 : 0);
-  // the lane's addresses are derived here, after the tile's K loop, not hoisted out of
-  // it as loop invariants (they would hold registers through the whole loop)
-  int ln = lane;
-  asm volatile("" : "+v"(ln));
-  const int j = ln / E::CHUNKS;                             // row inside an instruction
-  const int k = ln - j * E::CHUNKS;                         // 16-byte chunk of the row
-  const int col = o.n0 + k * 8;
-  const bool lane_ok = j < E::RPI && col < N;
-  const int e_w = uniform(C::WM * wm / E::RP);              // the pass of this wave's rows
-  // LDS byte offsets: this lane's first fragment write, and its first chunk read
-  const int wr = (C::WM * wm - e_w * E::RP + (ln & 15)) * E::ROW_BYTES + (C::WN * wn + 4 * (ln >> 4)) * 2;
-  const int rd = (wave * E::RPI + min(j, E::RPI - 1)) * E::ROW_BYTES + k * 16;
-  int out = (j * N + col) * 2;                              // + the instruction's first row
-  asm volatile("" : "+v"(out));
-  // bf16 now: the packed tile takes half the registers of the fp32 one through the passes
-  uint2 packed[C::TI][C::TJ];
-#pragma unroll
-  for (int i = 0; i < C::TI; ++i)
-#pragma unroll
-    for (int jj = 0; jj < C::TJ; ++jj)
-      packed[i][jj] = make_uint2(bf16x2_rne(acc[i][jj][0], acc[i][jj][1]),
-                                 bf16x2_rne(acc[i][jj][2], acc[i][jj][3]));
-#pragma unroll
-  for (int e = 0; e < E::EP; ++e) {
-    stage_barrier();                      // every wave is done reading the stage
-    if (e == e_w) {
-#pragma unroll
-      for (int i = 0; i < C::TI; ++i)
-#pragma unroll
-        for (int jj = 0; jj < C::TJ; ++jj)
-          *(uint2*)(st + wr + 16 * i * E::ROW_BYTES + 32 * jj) = packed[i][jj];
-    }
-    wait_lgkm0();                         // the writes are in LDS
-    stage_barrier();
-    // which lanes store, per instruction s (its rows are the pass rows r0 .. r0+RPI-1)
-    bool ok[E::SPP];
-#pragma unroll
-    for (int s = 0; s < E::SPP; ++s) {
-      const int r0 = (s * C::W + wave) * E::RPI;
-      const int row0 = e * E::RP + r0;                      // inside the tile
-      ok[s] = lane_ok && r0 + j < E::RP && j < o.rows - row0;
-      if (KIND == kContiguous) {
-        // a row is written if it and its 128-row block's first row name the group
-        int gi = -1;
-#pragma unroll
-        for (int u = 0; u < E::RPI; ++u) {
-          const int mu = row0 + u;
-          const int lead = mu < kAlignM ? o.lead0 : o.lead1;
-          const int gu = mu < o.rows && lead == o.g ? load_uniform(p.group_idx, o.a_row0 + mu) : -1;
-          if (j == u) gi = gu;
-        }
-        ok[s] = ok[s] && gi == o.g;
-      }
-    }
-    uint4 v[E::SPP];
-#pragma unroll
-    for (int s = 0; s < E::SPP; ++s) {
-      int at = rd + s * C::W * E::RPI * E::ROW_BYTES;
-      if ((s + 1) * C::W * E::RPI > E::RP) at = min(at, (E::RP - 1) * E::ROW_BYTES + k * 16);
-      v[s] = *(const uint4*)(st + at);
-    }
-    if (fast) {
-#pragma unroll
-      for (int s = 0; s < E::SPP; ++s) {
-        const int row0 = e * E::RP + (s * C::W + wave) * E::RPI;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v[s]), rc,
-                                               ok[s] ? out + row0 * N * 2 : kPastTile, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < E::SPP; ++s) {
-        if (!ok[s]) continue;
-        const int row0 = e * E::RP + (s * C::W + wave) * E::RPI;
-        uint16_t* dst = p.C + (size_t)(o.a_row0 + row0 + j) * N + col;
-        const uint32_t w[4] = {v[s].x, v[s].y, v[s].z, v[s].w};
-#pragma unroll
-        for (int x = 0; x < 8; ++x)
-          if (col + x < N) dst[x] = (uint16_t)(w[x >> 1] >> ((x & 1) * 16));
-      }
-    }
-  }
-  if (!fast) wait_vmcnt<0>();
-  return fast;
-}
-
-// The direct epilogue (dense and masked forms): no LDS and no barrier.  Lane (l16, q) of
+// The epilogue stores from registers: no LDS and no barrier.  Lane (l16, q) of
 // a wave holds columns 4q .. 4q+3 of row l16 of every 16x16 fragment.  For fragments j
 // and j+1, one v_permlane16_swap per packed bf16 word exchanges the odd 16-lane groups of
 // fragment j with the even ones of fragment j+1, after which lane (l16, q) holds the 8
 // consecutive columns 16(j + (q & 1)) + 8(q >> 1) .. +7 of its row: one 16-byte store, a
 // store instruction covering 16 rows x 64 bytes.  An odd last fragment is stored 8 bytes
 // per lane.  Fast form (N a multiple of 8): a fixed count of buffer stores per wave
-// (Epi::direct_stores), chunks outside the tile's rows or columns dropped by an offset
+// (direct_stores), chunks outside the tile's rows or columns dropped by an offset
 // past the buffer's range; otherwise element-wise stores and a full wait at the end.
+// Contiguous form: a row is stored only if it and its 128-row block's first row name the
+// tile's group; the rows' group indices come from the LDS slot the tile's first K block
+// filled (one 4-byte read per lane and fragment row).
 template <class C>
 constexpr int direct_stores() {
   return C::TI * ((C::TJ + 1) / 2);
 }
 
-template <class C>
+template <int KIND, class C>
 __device__ __forceinline__ bool store_tile_direct(const v4f (&acc)[C::TI][C::TJ],
                                                   const GemmArgs& p, const TileOut& o, int wm,
-                                                  int wn, int lane) {
+                                                  int wn, int lane, const int32_t* gl) {
   const int N = p.N;
   const bool fast = (N & 7) == 0 && (long)C::BM * N * 2 < (long)kPastTile;
   int ln = lane;
@@ -722,7 +614,13 @@ __device__ __forceinline__ bool store_tile_direct(const v4f (&acc)[C::TI][C::TJ]
 #pragma unroll
     for (int i = 0; i < C::TI; ++i) {
       const int r = row_w + 16 * i;
-      const bool row_ok = r < o.rows;
+      bool row_ok = r < o.rows;
+      if (KIND == kContiguous) {
+        // a row is written if it and its 128-row block's first row name the group (the
+        // rows' group indices were copied into LDS with the tile's first K block)
+        const int lead = r < kAlignM ? o.lead0 : o.lead1;
+        row_ok = row_ok && lead == o.g && gl[min(r, C::BM - 1)] == o.g;
+      }
       const int row_off = r * N;
 #pragma unroll
       for (int j = 0; j + 1 < C::TJ; j += 2) {
@@ -752,6 +650,10 @@ __device__ __forceinline__ bool store_tile_direct(const v4f (&acc)[C::TI][C::TJ]
     for (int i = 0; i < C::TI; ++i) {
       const int r = row_w + 16 * i;
       if (r >= o.rows) continue;
+      if (KIND == kContiguous) {
+        const int lead = r < kAlignM ? o.lead0 : o.lead1;
+        if (lead != o.g || gl[r] != o.g) continue;
+      }
       uint16_t* crow = p.C + (size_t)(o.a_row0 + r) * N;
 #pragma unroll
       for (int j = 0; j < C::TJ; ++j) {
@@ -885,19 +787,15 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
                                          int nwork) {
   constexpr int TI = C::TI, TJ = C::TJ;
   constexpr int STAGES = C::STAGES;
-  using E = Epi<C>;
-  // the contiguous form goes through LDS (its row checks read group indices per row);
-  // the others store from registers
-  constexpr bool DIRECT = KIND != kContiguous;
-  constexpr int NST = DIRECT ? direct_stores<C>() : E::NST;
+  constexpr int NST = direct_stores<C>();   // epilogue stores per wave
   static_assert((STAGES - 2) * (C::PER_STAGE + 1) + 1 + (STAGES - 1) * NST < 64, "vmcnt range");
   // copy-only waves: they store nothing, so their waits never count epilogue stores
   constexpr bool SPEC = C::XW > 0;
-  static_assert(!SPEC || DIRECT, "copy-only waves with the register epilogue only");
   const int nkb = p.nkb;
   const int wave = c.wave;
   const int cw = c.cw;
   const bool computes = !SPEC || wave < C::W;
+  constexpr bool GI = KIND == kContiguous;
 
   // w: the item being multiplied; wx: the next one, whose first K blocks are copied
   // during w's last steps (when every item has at least STAGES-1 K blocks; otherwise
@@ -910,6 +808,7 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
   Work wx = w;
   next_work<KIND, C, APP>(p, wx, G, nwork, c.lane);
   TileCtx cx = c;
+  cx.gslot = c.gslot ^ 1;
   if (wx.t < nwork) work_ctx(cx, p, wx);
   const bool cross = nkb >= STAGES - 1;
 
@@ -930,7 +829,7 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
     const int epi_n = stored && !SPEC ? 1 : 0;
     if (fill) {
       for (int f = 0; f < STAGES - 1 && f < nkb; ++f) {
-        issue_stage<C, true>(cp + sn * C::STAGE_BYTES, c, f, cp + STAGES * C::STAGE_BYTES);
+        issue_stage<C, true, GI>(cp + sn * C::STAGE_BYTES, c, f, cp, p.group_idx);
         sn = sn + 1 == STAGES ? 0 : sn + 1;
       }
     }
@@ -939,8 +838,7 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
     for (; kb + STAGES - 1 < nkb; ++kb) {
       wait_copies_epi<C, NST>(cw, STAGES - 2, kb <= STAGES - 2 ? epi_n : 0);
       stage_barrier();
-      issue_stage<C, true>(cp + sn * C::STAGE_BYTES, c, kb + STAGES - 1,
-                           cp + STAGES * C::STAGE_BYTES);
+      issue_stage<C, true, GI>(cp + sn * C::STAGE_BYTES, c, kb + STAGES - 1, cp, p.group_idx);
       sn = sn + 1 == STAGES ? 0 : sn + 1;
       if (computes) compute_stage<C>(rd + sc * C::STAGE_BYTES, c, acc);
       sc = sc + 1 == STAGES ? 0 : sc + 1;
@@ -952,8 +850,8 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
                               kb <= STAGES - 2 ? epi_n : 0);
       stage_barrier();
       if (more) {
-        issue_stage<C, true>(cp + sn * C::STAGE_BYTES, cx, kb + STAGES - 1 - nkb,
-                             cp + STAGES * C::STAGE_BYTES);
+        issue_stage<C, true, GI>(cp + sn * C::STAGE_BYTES, cx, kb + STAGES - 1 - nkb, cp,
+                                 p.group_idx);
         sn = sn + 1 == STAGES ? 0 : sn + 1;
       }
       if (computes) compute_stage<C>(rd + sc * C::STAGE_BYTES, c, acc);
@@ -965,11 +863,8 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
         o.g = w.pass == 0 ? w.tr.g : w.tr.g2;
         o.lead0 = w.tr.lead0;
         o.lead1 = w.tr.lead1;
-        if constexpr (DIRECT)
-          fast = store_tile_direct<C>(acc, p, o, c.wm, c.wn, c.lane);
-        else
-          fast = store_tile_staged<KIND, C>(rd + sc * C::STAGE_BYTES, acc, p, o, wave, c.lane,
-                                            c.wm, c.wn, c.q, c.l16);
+        fast = store_tile_direct<KIND, C>(acc, p, o, c.wm, c.wn, c.lane,
+                                          (const int32_t*)(rd + C::GI_OFF + c.gslot * (C::BM * 4)));
       }
       sc = sc + 1 == STAGES ? 0 : sc + 1;
     }
@@ -982,6 +877,7 @@ __device__ __forceinline__ void tile_walk(uint8_t* __restrict__ cp, uint8_t* __r
     fill = !cross;
     w = wx;
     c = cx;
+    cx.gslot = c.gslot ^ 1;
     next_work<KIND, C, APP>(p, wx, G, nwork, c.lane);
     if (wx.t < nwork) work_ctx(cx, p, wx);
   }
@@ -1011,6 +907,7 @@ gemm_fp8_kernel(GemmArgs p) {
   c.lane = tid & 63;
   c.wave = uniform(tid >> 6);
   c.cw = c.wave - C::CW0;
+  c.gslot = 0;
   c.wm = c.wave / C::WAVES_N;
   c.wn = c.wave - c.wm * C::WAVES_N;
   c.q = c.lane >> 4;
