@@ -49,6 +49,11 @@
  *     null stream), never synchronises, and performs no host readback, so it may be
  *     captured in a HIP graph.  Faults inside kernels surface at the caller's next
  *     synchronisation.  Results are deterministic: the same inputs give the same bits.
+ *   - Range: each K block's partial, the factor sA*sB and the accumulator are fp32, so a
+ *     result is exact up to fp32 rounding as long as they stay inside the fp32 range.
+ *     Scales from the quantisation calls below keep sA*sB finite whenever the two
+ *     blocks' maxima multiply to less than about 6.8e43 (448^2 * FLT_MAX); beyond that
+ *     the factor is +inf and the element becomes +-inf or NaN (0 * inf, inf - inf).
  *   - Workspace: device memory the caller lends for split-K partial sums, at least
  *     dg_workspace_bytes(...) bytes, 16-byte aligned.  It must be zero filled before
  *     its first use; every call leaves it zero filled again (a zero word marks a partial
