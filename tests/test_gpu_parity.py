@@ -554,6 +554,45 @@ def test_graph_capture_replays_with_new_counts():
         assert_within_tolerance(got_d, ref_dense, np.ones_like(got_d, bool), "graph replay dense")
 
 
+def test_graph_capture_contiguous_new_routing():
+    """The contiguous call captured once in a HIP graph and replayed with new group
+    indices written between replays (groups of other sizes and order, 256-row tiles that
+    straddle two groups, a padding block of index -1, one group for every row): every
+    replay matches the oracle and leaves the padding rows untouched."""
+    from moe_grouped_gemm_lhs_amd import binding as dg
+    G, M, N, K = 4, 1024, 384, 1024
+    p = I.make_contiguous([256, 128, 384, 256], N, K, seed=48)
+    A, sA, B, sB = gu.device_operands(p)
+    gi = torch.from_numpy(p.group_idx.copy()).to(gu.DEV)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=gu.DEV)
+    sentinel = int(np.uint16(SENTINEL).view(np.int16))
+    gu.say("[case] graph capture contiguous")
+    dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, gi, C)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        dg.dg_grouped_gemm_fp8_contiguous(A, sA, B, sB, gi, C)
+    torch.cuda.synchronize()
+    layouts = [I.group_sizes_to_idx([256, 128, 384, 256]),
+               np.repeat(np.array([2, 0, 3, 1], np.int32), [128, 512, 128, 256]),
+               np.repeat(np.array([1, -1, 0, 3], np.int32), [256, 128, 384, 256]),
+               np.full(M, 3, np.int32)]
+    for gl in layouts:
+        gl = np.ascontiguousarray(gl, dtype=np.int32)
+        gu.say(f"[case] graph replay contiguous, groups {np.unique(gl).tolist()}")
+        gi.copy_(torch.from_numpy(gl))
+        C.view(torch.int16).fill_(sentinel)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = C.view(torch.int16).cpu().numpy().view(np.uint16)
+        ref = gu.oracle_full(p, group_idx=gl)
+        w = np.repeat(gu.written_rows(p, group_idx=gl)[:, None], N, axis=1)
+        assert_within_tolerance(got, ref, w, f"graph replay contiguous {np.unique(gl)}")
+
+
 def test_auto_workspace_on_side_streams():
     """Split-K decode calls without a workspace argument, launched on two side streams
     (neither the current stream) back to back and concurrently: each stream gets its own
