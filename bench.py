@@ -27,6 +27,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0         # MI355X dense FP8 MFMA (no sparsity)
+PEAK_SCLK_MHZ = 2400.0           # the engine clock the MFMA peak is quoted at
 
 
 def parse():
@@ -345,6 +346,10 @@ def measure(name, args, torch, np, dg, I, dev, headline=False):
                                                             args.steps)
     if headline:
         out["sclk_mhz"] = None if args.no_sclk else sclk_while_running(torch, calls[dom], 2.0)
+        if not hbm_bound and out["sclk_mhz"]:
+            # the same fraction against the MFMA peak at the clock the GPU held meanwhile
+            peak_held = FP8_PEAK_TFLOPS * out["sclk_mhz"]["median"] / PEAK_SCLK_MHZ
+            roof["frac_at_sclk"] = round(achieved / peak_held, 4)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(problems, calls, args.cpu_budget_s, hbm_bound)
     return out
